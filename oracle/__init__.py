@@ -1,0 +1,185 @@
+"""fp64 CPU oracle for banded sparse self-attention forward (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg import this package.  It shares no code with the HIP library
+(``sparse_long_sequence_banded_amd``) and neither imports the other; the only code both sides
+use is the seeded input generator package ``workloads``.
+
+The arithmetic lives in ``longattn_oracle.c`` (plain C, fp64, OpenMP); what it computes and
+which passage each step follows is written at the top of that file.  Every function is pinned
+by the CPU tests (dense brute force, library full/causal attention, the Big Bird worked window
+example, closed-form counts and invariants); none is left "parity unpinned".
+"""
+
+import contextlib
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "longattn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblongattn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (IEEE fp64: no fast-math) into ``liblongattn_oracle.so``."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(lib):
+    lib.longattn_oracle_forward.restype = ctypes.c_int
+    lib.longattn_oracle_forward.argtypes = [
+        _I64, _I64, _I64, _I64, ctypes.c_double, _I64, _I64, _P, _P, _I64, _P, _P,
+        _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_int,
+    ]
+    lib.longattn_oracle_count.restype = ctypes.c_int
+    lib.longattn_oracle_count.argtypes = [
+        _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _P, ctypes.c_int,
+    ]
+    lib.longattn_oracle_row_set.restype = ctypes.c_int64
+    lib.longattn_oracle_row_set.argtypes = [
+        _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64,
+        _I64, _P,
+    ]
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+@contextlib.contextmanager
+def substituted_library(path: str):
+    """Temporarily route every oracle call to another build of the oracle source.
+
+    Used only by the test that plants deliberate mistakes in a copy of the C source and checks
+    that the pins catch each one.
+    """
+    global _lib
+    _load()
+    saved = _lib
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _struct_args(B, H, n, win_left, win_right, dilation, global_idx, key_pad, layout, block,
+                 max_kb):
+    dil = _c(dilation, np.int32)
+    gi = _c(global_idx, np.int32)
+    kp = _c(key_pad, np.uint8)
+    lay = _c(layout, np.int32)
+    g = 0 if gi is None else int(gi.shape[-1])
+    if gi is not None:
+        assert gi.shape == (B, g), gi.shape
+    if dil is not None:
+        assert dil.shape == (H,), dil.shape
+    if kp is not None:
+        assert kp.shape == (B, n), kp.shape
+    if lay is not None:
+        assert block > 0 and n % block == 0
+        assert lay.shape == (H, n // block, max_kb), lay.shape
+    keep = (dil, gi, kp, lay)
+    return keep, (win_left, win_right, _ptr(dil), _ptr(gi), g, _ptr(kp), _ptr(lay), block, max_kb)
+
+
+def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, win_left: int,
+            win_right: int, dilation=None, global_idx=None, key_pad=None, layout=None,
+            block: int = 0, max_kb: int = 0, nthreads: int = 0
+            ) -> Tuple[np.ndarray, np.ndarray, int]:
+    """Returns (out [B,H,n,d] fp64, lse [B,H,n] fp64, E)."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, H, n, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    keep, sargs = _struct_args(B, H, n, win_left, win_right, dilation, global_idx, key_pad,
+                               layout, block, max_kb)
+    out = np.empty_like(q)
+    lse = np.empty((B, H, n), dtype=np.float64)
+    E = ctypes.c_int64(0)
+    w_l, w_r, dil, gi, g, kp, lay, blk, mkb = sargs
+    rc = _load().longattn_oracle_forward(
+        B, H, n, d, float(scale), w_l, w_r, dil, gi, g, kp, lay, blk, mkb,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), ctypes.byref(E), int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out, lse, int(E.value)
+
+
+def count(B: int, H: int, n: int, *, win_left: int, win_right: int, dilation=None,
+          global_idx=None, key_pad=None, layout=None, block: int = 0, max_kb: int = 0,
+          nthreads: int = 0) -> int:
+    """E: the number of useful (query, key) score entries."""
+    keep, sargs = _struct_args(B, H, n, win_left, win_right, dilation, global_idx, key_pad,
+                               layout, block, max_kb)
+    E = ctypes.c_int64(0)
+    w_l, w_r, dil, gi, g, kp, lay, blk, mkb = sargs
+    rc = _load().longattn_oracle_count(B, H, n, w_l, w_r, dil, gi, g, kp, lay, blk, mkb,
+                                       ctypes.byref(E), int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return int(E.value)
+
+
+def row_set(B: int, H: int, n: int, b: int, h: int, i: int, *, win_left: int, win_right: int,
+            dilation=None, global_idx=None, key_pad=None, layout=None, block: int = 0,
+            max_kb: int = 0) -> np.ndarray:
+    """The ascending allowed key set S(b, h, i)."""
+    keep, sargs = _struct_args(B, H, n, win_left, win_right, dilation, global_idx, key_pad,
+                               layout, block, max_kb)
+    buf = np.empty(max(n, 1), dtype=np.int32)
+    w_l, w_r, dil, gi, g, kp, lay, blk, mkb = sargs
+    cnt = _load().longattn_oracle_row_set(B, H, n, w_l, w_r, dil, gi, g, kp, lay, blk, mkb,
+                                          b, h, i, _ptr(buf))
+    del keep
+    if cnt < 0:
+        raise ValueError(f"oracle rejected the arguments (code {cnt})")
+    return buf[:cnt].copy()
+
+
+def forward_inputs(inp, nthreads: int = 0):
+    """Oracle forward on a ``workloads.Inputs`` instance (exact fp64 widening of its values)."""
+    return forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), scale=inp.scale,
+                   win_left=inp.win_left, win_right=inp.win_right, dilation=inp.dilation,
+                   global_idx=inp.global_idx, key_pad=inp.key_pad, layout=inp.layout,
+                   block=inp.block, max_kb=inp.max_kb, nthreads=nthreads)
+
+
+def count_inputs(inp, nthreads: int = 0) -> int:
+    return count(inp.batch, inp.heads, inp.n, win_left=inp.win_left, win_right=inp.win_right,
+                 dilation=inp.dilation, global_idx=inp.global_idx, key_pad=inp.key_pad,
+                 layout=inp.layout, block=inp.block, max_kb=inp.max_kb, nthreads=nthreads)

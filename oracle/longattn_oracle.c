@@ -1,0 +1,272 @@
+/*
+ * fp64 CPU oracle for the forward pass of banded sparse self-attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct definition that the
+ * GPU library is checked against.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  It shares no code, header, table or helper with the HIP library,
+ * and the HIP library never calls it.
+ *
+ * What it computes.  Attention restricted to a sparse key set is exact masked softmax
+ * attention; nothing is approximated.  The pages describe the pattern as a directed graph
+ * whose edges are the allowed (query, key) pairs (Big Bird reading notes, section 3.1), built
+ * as the union of a local window, global tokens and random keys (same notes, section 3.3).
+ * For batch b, head h and query row i:
+ *
+ *   1. Allowed set A.
+ *      - If i is a global token of sample b, A = every position: a global token attends the
+ *        whole sequence (Longformer hub page, section 2; Big Bird notes, section 3.2.3).
+ *      - Otherwise A is the union of
+ *          Band(i)  = { i + dil[h]*t : t in [-win_left, win_right] }, cut to [0, n)
+ *                     (window around the query, Big Bird notes section 3.2.1; the window
+ *                     skips tokens like a dilated convolution when dil > 1, Longformer hub
+ *                     page section 2),
+ *          G_b      = the global tokens, which every position attends,
+ *          Layout   = every key of the blocks listed for (h, block of i) in the block
+ *                     layout (random and sliding blocks, Big Bird notes section 3.2.2).
+ *        win_left = win_right = -1 switches the band off.
+ *   2. Padded keys are removed: S = A minus { j : key_pad[b][j] != 0 } (the Longformer hub
+ *      page, section 5: mask value 0 marks padding).  A key is counted once even when it is
+ *      in several of the sets (a graph edge exists or not).
+ *   3. E += |S| (the number of useful score entries).
+ *   4. If S is empty: out = 0 and lse = -infinity.
+ *   5. s_j = scale * sum_c q[i][c] * k[j][c] for j in S, ascending c, in fp64.
+ *   6. m = max s_j, w_j = exp(s_j - m), l = sum w_j, out = (sum_j w_j v[j]) / l and
+ *      lse = m + log(l); sums run over S in ascending key order.
+ *
+ * Layout of every tensor: contiguous [batch][heads][n][d] (q, k, v, out) and
+ * [batch][heads][n] (lse).  All pointers are host pointers.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = -1, ORACLE_NO_MEMORY = -2 };
+
+static int cmp_i32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+static int64_t floor_div(int64_t a, int64_t b) { /* b > 0 */
+  int64_t q = a / b;
+  if ((a % b != 0) && (a < 0)) q -= 1;
+  return q;
+}
+
+typedef struct {
+  int64_t B, H, n, d;
+  int64_t win_left, win_right;
+  const int32_t* dilation;
+  const int32_t* global_idx;
+  int64_t n_global;
+  const uint8_t* key_pad;
+  const int32_t* layout;
+  int64_t block, max_kb;
+} problem;
+
+static int check(const problem* p) {
+  if (p->B < 0 || p->H < 0 || p->n < 0 || p->d < 0 || p->n_global < 0) return ORACLE_BAD_ARG;
+  int band_off = (p->win_left == -1 && p->win_right == -1);
+  if (!band_off && (p->win_left < 0 || p->win_right < 0)) return ORACLE_BAD_ARG;
+  if (p->dilation)
+    for (int64_t h = 0; h < p->H; ++h)
+      if (p->dilation[h] < 1) return ORACLE_BAD_ARG;
+  if (p->n_global > 0) {
+    if (!p->global_idx) return ORACLE_BAD_ARG;
+    for (int64_t t = 0; t < p->B * p->n_global; ++t)
+      if (p->global_idx[t] < 0 || p->global_idx[t] >= p->n) return ORACLE_BAD_ARG;
+  }
+  if (p->layout) {
+    if (p->block < 1 || p->max_kb < 0 || (p->n % p->block) != 0) return ORACLE_BAD_ARG;
+    int64_t nb = p->n / p->block;
+    for (int64_t t = 0; t < p->H * nb * p->max_kb; ++t)
+      if (p->layout[t] < -1 || p->layout[t] >= nb) return ORACLE_BAD_ARG;
+  }
+  return ORACLE_OK;
+}
+
+/* Per-thread scratch: an epoch-stamped marker per position so a key in several sets is
+ * listed once, the key list itself and its scores. */
+typedef struct {
+  int64_t* mark;
+  int64_t epoch;
+  int32_t* keys;
+  int64_t cnt;
+  double* s;
+} scratch;
+
+static void add_key(scratch* w, const problem* p, int64_t b, int64_t j) {
+  if (w->mark[j] == w->epoch) return;
+  w->mark[j] = w->epoch;
+  if (p->key_pad && p->key_pad[b * p->n + j]) return; /* padded keys are never attended */
+  w->keys[w->cnt++] = (int32_t)j;
+}
+
+/* Builds S(b, h, i) in w->keys (ascending).  is_global[b*n + i] marks global rows. */
+static void build_set(scratch* w, const problem* p, const uint8_t* is_global, int64_t b,
+                      int64_t h, int64_t i) {
+  w->epoch += 1;
+  w->cnt = 0;
+  if (is_global && is_global[b * p->n + i]) {
+    for (int64_t j = 0; j < p->n; ++j) add_key(w, p, b, j);
+    return; /* already ascending */
+  }
+  if (!(p->win_left == -1 && p->win_right == -1)) {
+    int64_t dil = p->dilation ? p->dilation[h] : 1;
+    /* keys i + dil*t with t in [-win_left, win_right] that fall inside [0, n) */
+    int64_t t_lo = -p->win_left, t_hi = p->win_right;
+    int64_t t_min_in = -floor_div(i, dil);           /* smallest t with i + dil*t >= 0 */
+    int64_t t_max_in = floor_div(p->n - 1 - i, dil); /* largest t with i + dil*t <= n-1 */
+    if (t_lo < t_min_in) t_lo = t_min_in;
+    if (t_hi > t_max_in) t_hi = t_max_in;
+    for (int64_t t = t_lo; t <= t_hi; ++t) add_key(w, p, b, i + dil * t);
+  }
+  for (int64_t c = 0; c < p->n_global; ++c) add_key(w, p, b, p->global_idx[b * p->n_global + c]);
+  if (p->layout) {
+    int64_t nb = p->n / p->block;
+    const int32_t* row = p->layout + (h * nb + i / p->block) * p->max_kb;
+    for (int64_t s = 0; s < p->max_kb; ++s) {
+      if (row[s] < 0) continue;
+      for (int64_t j = (int64_t)row[s] * p->block; j < ((int64_t)row[s] + 1) * p->block; ++j)
+        add_key(w, p, b, j);
+    }
+  }
+  qsort(w->keys, (size_t)w->cnt, sizeof(int32_t), cmp_i32);
+}
+
+static int run(const problem* p, double scale, const double* q, const double* k,
+               const double* v, double* out, double* lse, int64_t* E_out, int nthreads) {
+  int rc = check(p);
+  if (rc != ORACLE_OK) return rc;
+  int64_t rows = p->B * p->H * p->n;
+  uint8_t* is_global = NULL;
+  if (p->n_global > 0 && p->B * p->n > 0) {
+    is_global = (uint8_t*)calloc((size_t)(p->B * p->n), 1);
+    if (!is_global) return ORACLE_NO_MEMORY;
+    for (int64_t b = 0; b < p->B; ++b)
+      for (int64_t c = 0; c < p->n_global; ++c)
+        is_global[b * p->n + p->global_idx[b * p->n_global + c]] = 1;
+  }
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  int64_t E = 0;
+  int failed = 0;
+#pragma omp parallel num_threads(nthreads) reduction(+ : E) reduction(| : failed)
+  {
+    scratch w;
+    size_t cap = (size_t)(p->n > 0 ? p->n : 1);
+    w.mark = (int64_t*)malloc(cap * sizeof(int64_t));
+    w.keys = (int32_t*)malloc(cap * sizeof(int32_t));
+    w.s = (double*)malloc(cap * sizeof(double));
+    w.epoch = 0;
+    if (!w.mark || !w.keys || !w.s) failed = 1;
+    if (!failed) {
+      for (size_t j = 0; j < cap; ++j) w.mark[j] = 0;
+    }
+#pragma omp for schedule(dynamic, 32)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (failed) continue;
+      int64_t i = r % p->n, bh = r / p->n, h = bh % p->H, b = bh / p->H;
+      build_set(&w, p, is_global, b, h, i);
+      E += w.cnt;
+      if (!q) continue; /* counting only */
+      const double* qi = q + r * p->d;
+      double* oi = out + r * p->d;
+      const double* kb = k + bh * p->n * p->d;
+      const double* vb = v + bh * p->n * p->d;
+      if (w.cnt == 0) {
+        for (int64_t c = 0; c < p->d; ++c) oi[c] = 0.0;
+        if (lse) lse[r] = -INFINITY;
+        continue;
+      }
+      double m = -INFINITY;
+      for (int64_t t = 0; t < w.cnt; ++t) {
+        const double* kj = kb + (int64_t)w.keys[t] * p->d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < p->d; ++c) dot += qi[c] * kj[c];
+        w.s[t] = scale * dot;
+        if (w.s[t] > m) m = w.s[t];
+      }
+      double l = 0.0;
+      for (int64_t c = 0; c < p->d; ++c) oi[c] = 0.0;
+      for (int64_t t = 0; t < w.cnt; ++t) {
+        double wt = exp(w.s[t] - m);
+        l += wt;
+        const double* vj = vb + (int64_t)w.keys[t] * p->d;
+        for (int64_t c = 0; c < p->d; ++c) oi[c] += wt * vj[c];
+      }
+      for (int64_t c = 0; c < p->d; ++c) oi[c] /= l;
+      if (lse) lse[r] = m + log(l);
+    }
+    free(w.mark);
+    free(w.keys);
+    free(w.s);
+  }
+  free(is_global);
+  if (failed) return ORACLE_NO_MEMORY;
+  if (E_out) *E_out = E;
+  return ORACLE_OK;
+}
+
+/* Forward pass.  q, k, v, out: [B][H][n][d] fp64; lse: [B][H][n] fp64 or NULL.
+ * dilation: [H] or NULL (all 1).  global_idx: [B][n_global], each in [0, n).
+ * key_pad: [B][n] (nonzero = padded key) or NULL.  layout: [H][n/block][max_kb] block ids,
+ * -1 = unused slot, or NULL.  E_out: receives the number of useful score entries.
+ * nthreads <= 0 uses OpenMP's default.  Returns 0, or a negative code on bad arguments. */
+int longattn_oracle_forward(int64_t B, int64_t H, int64_t n, int64_t d, double scale,
+                            int64_t win_left, int64_t win_right, const int32_t* dilation,
+                            const int32_t* global_idx, int64_t n_global, const uint8_t* key_pad,
+                            const int32_t* layout, int64_t block, int64_t max_kb,
+                            const double* q, const double* k, const double* v, double* out,
+                            double* lse, int64_t* E_out, int nthreads) {
+  problem p = {B, H, n, d, win_left, win_right, dilation, global_idx, n_global,
+               key_pad, layout, block, max_kb};
+  if (!q || !k || !v || !out) return ORACLE_BAD_ARG;
+  return run(&p, scale, q, k, v, out, lse, E_out, nthreads);
+}
+
+/* Number of useful score entries E = sum over (b, h, i) of |S(b, h, i)|, no arithmetic. */
+int longattn_oracle_count(int64_t B, int64_t H, int64_t n, int64_t win_left, int64_t win_right,
+                          const int32_t* dilation, const int32_t* global_idx, int64_t n_global,
+                          const uint8_t* key_pad, const int32_t* layout, int64_t block,
+                          int64_t max_kb, int64_t* E_out, int nthreads) {
+  problem p = {B, H, n, 0, win_left, win_right, dilation, global_idx, n_global,
+               key_pad, layout, block, max_kb};
+  return run(&p, 0.0, NULL, NULL, NULL, NULL, NULL, E_out, nthreads);
+}
+
+/* The allowed key set of one query row, ascending, written to keys_out (capacity n).
+ * Returns the set size, or a negative code on bad arguments. */
+int64_t longattn_oracle_row_set(int64_t B, int64_t H, int64_t n, int64_t win_left,
+                                int64_t win_right, const int32_t* dilation,
+                                const int32_t* global_idx, int64_t n_global,
+                                const uint8_t* key_pad, const int32_t* layout, int64_t block,
+                                int64_t max_kb, int64_t b, int64_t h, int64_t i,
+                                int32_t* keys_out) {
+  problem p = {B, H, n, 0, win_left, win_right, dilation, global_idx, n_global,
+               key_pad, layout, block, max_kb};
+  int rc = check(&p);
+  if (rc != ORACLE_OK) return rc;
+  if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= n) return ORACLE_BAD_ARG;
+  uint8_t* is_global = NULL;
+  if (n_global > 0) {
+    is_global = (uint8_t*)calloc((size_t)(B * n), 1);
+    if (!is_global) return ORACLE_NO_MEMORY;
+    for (int64_t bb = 0; bb < B; ++bb)
+      for (int64_t c = 0; c < n_global; ++c) is_global[bb * n + global_idx[bb * n_global + c]] = 1;
+  }
+  scratch w;
+  w.mark = (int64_t*)calloc((size_t)n, sizeof(int64_t));
+  w.keys = keys_out;
+  w.s = NULL;
+  w.epoch = 0;
+  if (!w.mark) {
+    free(is_global);
+    return ORACLE_NO_MEMORY;
+  }
+  build_set(&w, &p, is_global, b, h, i);
+  free(w.mark);
+  free(is_global);
+  return w.cnt;
+}

@@ -1,0 +1,94 @@
+"""The pins are sharp enough: each planted mistake in a copy of the oracle fails at least one.
+
+Every mutant is a one-line edit of the oracle's C source of the kind a careless port would
+make (a dropped term, a wrong sign, a swapped operand or index).  It is built into a temporary
+library, every oracle call is routed to it, and the pin tests of ``test_oracle`` are run
+against it; at least one must fail.  Mutants are chosen so they stay in bounds (none can make
+the oracle read outside its arrays).
+"""
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "longattn_oracle.c")
+
+MUTANTS = {
+    "window_extents_swapped": ("int64_t t_lo = -p->win_left, t_hi = p->win_right;",
+                               "int64_t t_lo = -p->win_right, t_hi = p->win_left;"),
+    "dilation_ignored": ("int64_t dil = p->dilation ? p->dilation[h] : 1;", "int64_t dil = 1;"),
+    "band_right_edge_short": ("int64_t t_max_in = floor_div(p->n - 1 - i, dil);",
+                              "int64_t t_max_in = floor_div(p->n - 2 - i, dil);"),
+    "padding_ignored": ("  if (p->key_pad && p->key_pad[b * p->n + j]) return;", ""),
+    "global_rows_not_full": ("if (is_global && is_global[b * p->n + i]) {", "if (0) {"),
+    "global_columns_dropped": (
+        "for (int64_t c = 0; c < p->n_global; ++c) add_key(w, p, b, p->global_idx[b * p->n_global + c]);",
+        ""),
+    "softmax_sign_flipped": ("double wt = exp(w.s[t] - m);", "double wt = exp(m - w.s[t]);"),
+    "scale_dropped": ("w.s[t] = scale * dot;", "w.s[t] = dot;"),
+    "values_read_from_keys": ("const double* vj = vb + (int64_t)w.keys[t] * p->d;",
+                              "const double* vj = kb + (int64_t)w.keys[t] * p->d;"),
+    "lse_without_log": ("if (lse) lse[r] = m + log(l);", "if (lse) lse[r] = m + l;"),
+    "no_normalisation": ("for (int64_t c = 0; c < p->d; ++c) oi[c] /= l;", ""),
+    "empty_row_lse_zero": ("if (lse) lse[r] = -INFINITY;", "if (lse) lse[r] = 0.0;"),
+    "layout_block_of_key_not_query": (
+        "const int32_t* row = p->layout + (h * nb + i / p->block) * p->max_kb;",
+        "const int32_t* row = p->layout + (h * nb + (i % nb)) * p->max_kb;"),
+    "layout_block_width_off": (
+        "for (int64_t j = (int64_t)row[s] * p->block; j < ((int64_t)row[s] + 1) * p->block; ++j)",
+        "for (int64_t j = (int64_t)row[s] * p->block; j < ((int64_t)row[s] + 1) * p->block - 1; ++j)"),
+    "query_row_of_other_head": ("const double* qi = q + r * p->d;",
+                                "const double* qi = q + (r % p->n) * p->d;"),
+}
+
+PINS = [
+    lambda: [pins.test_oracle_matches_dense_brute_force(c) for c in pins.CASES],
+    lambda: pins.test_window_covering_sequence_is_full_attention(37, 8),
+    lambda: pins.test_causal_window_covering_sequence_is_causal_attention(50),
+    pins.test_layout_listing_every_block_is_full_attention,
+    pins.test_softmax_rows_sum_to_one,
+    pins.test_keys_outside_the_set_contribute_exactly_zero,
+    pins.test_bigbird_worked_window_example,
+    pins.test_window_zero_returns_v_exactly,
+    pins.test_zero_keys_give_the_mean_of_values,
+    lambda: pins.test_band_count_closed_form(100, 7, 2),
+    lambda: pins.test_dilated_row_counts(101, 3, 4, 9),
+    pins.test_empty_rows_give_zero_output_and_minus_infinity_lse,
+    pins.test_bigbird_global_blocks_as_layout_or_as_global_tokens,
+    pins.test_global_rows_attend_every_unpadded_key_and_padding_wins,
+]
+
+
+def _caught(lib_path):
+    failures = 0
+    with oracle.substituted_library(lib_path):
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                failures += 1
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(mutant_c), "-lm"], check=True, capture_output=True)
+    assert _caught(str(so)) >= 1, f"no pin catches the planted mistake {name}"
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    so = tmp_path / "libcopy.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    SRC, "-lm"], check=True, capture_output=True)
+    assert _caught(str(so)) == 0
