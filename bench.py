@@ -1,0 +1,200 @@
+"""Benchmark: useful TFLOP/s of the banded sparse attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one full forward pass (main sparse kernel, global-row partials, global-row combine)
+over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
+timed back to back between two device synchronisations.  Useful work is 4*d*E floating-point
+operations, E being the number of allowed (query, key) score entries counted by the library on
+the GPU.  Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "useful TFLOP/s + % bf16 MFMA peak, window attn fwd at n=4096/16384 (1 GPU)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+DEFAULT_WORKLOAD = "dilated_16k"
+MAIN_KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", "attn_mfma.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-gflop", type=float, default=64.0,
+                    help="fp64 work of the oracle sample (whole heads, at least one)")
+    return ap.parse_args()
+
+
+def _source_hash():
+    with open(MAIN_KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload):
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_main_kernel_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != _source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(inp, budget_gflop):
+    import oracle
+
+    E_head = []
+    for h in range(inp.heads):
+        E_head.append(oracle.count_inputs(inp.select_heads([h])))
+    flop_head = [4.0 * inp.d * e for e in E_head]
+    heads = []
+    tot = 0.0
+    for h in range(inp.heads):
+        if heads and tot + flop_head[h] > budget_gflop * 1e9:
+            break
+        heads.append(h)
+        tot += flop_head[h]
+    sub = inp.select_heads(heads)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    _, _, E = oracle.forward_inputs(sub, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": 4.0 * inp.d * E / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"heads {heads[0]}-{heads[-1]} of {inp.heads} (all rows), {E} entries, "
+                  f"{4.0 * inp.d * E / 1e9:.1f} GFLOP fp64 in {dt:.2f} s",
+    }
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the sparse attention path here has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_long_sequence_banded_amd as la
+    from workloads import make_inputs, workload
+    from workloads.torch_io import to_torch
+
+    w = workload(args.workload)
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    t = to_torch(inp, dev)
+    q, k, v = t["q"], t["k"], t["v"]
+    kw = dict(scale=inp.scale, win_left=inp.win_left, win_right=inp.win_right,
+              dilation=inp.dilation, global_idx=t["global_idx"], key_pad=t["key_pad"],
+              block_layout=t["layout"], block=inp.block)
+    E, E_global_rows = la.count_entries(q, **{k2: kw[k2] for k2 in kw if k2 != "scale"})
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    desc, keep = la.make_desc(q, **kw)
+    _, ws_bytes = la.longattn_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        la.forward(q, k, v, out=out, lse=lse, workspace=ws, stream=stream, **kw)
+    torch.cuda.synchronize()
+
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(la.LONGATTN_N_MARKS)]
+             for _ in range(args.steps)]
+    for row in marks:  # create the underlying events before their handles are used
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in marks]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        la.forward(q, k, v, out=out, lse=lse, workspace=ws, stream=stream, marks=handles[s], **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    spans = np.array([[marks[s][i].elapsed_time(marks[s][i + 1]) for i in range(3)]
+                      for s in range(args.steps)])  # ms
+    main_ms, part_ms, comb_ms = (float(x) for x in spans.mean(axis=0))
+    ms_per_step = elapsed * 1e3 / args.steps
+    useful_flop = 4.0 * inp.d * E
+    value = useful_flop / (ms_per_step * 1e-3) / 1e12
+
+    # main sparse kernel: useful work of the non-global rows (global rows are recomputed by the
+    # global-row kernels); algorithmic bytes = Q, K, V read once + O written once (+ lse)
+    elem = 2 if inp.dtype == "bf16" else 4
+    main_flop = 4.0 * inp.d * (E - E_global_rows)
+    main_tflops = main_flop / (main_ms * 1e-3) / 1e12
+    alg_bytes = 4.0 * inp.batch * inp.heads * inp.n * inp.d * elem + 4.0 * inp.batch * inp.heads * inp.n
+    traffic = _traffic(args.workload)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": inp.batch, "heads": inp.heads, "seq_len": inp.n, "head_dim": inp.d,
+            "win_left": inp.win_left, "win_right": inp.win_right,
+            "dilation": None if inp.dilation is None else inp.dilation.tolist(),
+            "n_global": inp.n_global, "block": inp.block,
+            "useful_entries": E, "useful_entries_global_rows": E_global_rows,
+            "description": w.note,
+        },
+        "pct_bf16_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernels_ms": {"main_sparse": round(main_ms, 5), "global_partial": round(part_ms, 5),
+                       "global_combine": round(comb_ms, 5)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_mfma_kernel (main sparse kernel)",
+            "achieved": round(main_tflops, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "roofline_hbm": {
+            "achieved": round(alg_bytes / (main_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(alg_bytes / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": alg_bytes,
+        },
+    }
+    rec["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline(inp, args.cpu_budget_gflop)
+    del keep
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * longattn — forward pass of banded sparse self-attention on AMD MI355X (gfx950).
+ *
+ * What one call computes.  For every batch sample b, head h and query row i, the output row
+ * is exact softmax attention of q[b,h,i] over the key set S(b,h,i), scaled by `scale`:
+ *
+ *   out[b,h,i] = sum_{j in S} softmax_j(scale * q_i . k_j) * v_j,
+ *   lse[b,h,i] = log sum_{j in S} exp(scale * q_i . k_j)       (natural log)
+ *
+ * S is the union of (each key counted once), minus the padded keys of sample b:
+ *   - the window i + dil[h]*t, t in [-win_left, win_right], cut to [0, n): a sliding window
+ *     around the query, symmetric as in Longformer or causal (win_right = 0) as in
+ *     sliding-window decoders (Longformer hub page, section 2; Big Bird reading notes,
+ *     section 3.2.1; SWAN-GPT summary, section 3.3).  With dil > 1 the window skips tokens
+ *     like a dilated convolution: the same number of keys over a span dil times wider
+ *     (Longformer hub page, section 2);
+ *   - the global tokens global_idx[b][*]: every position attends them, and a global token's
+ *     own row attends the whole sequence (Longformer hub page, section 2; Big Bird notes,
+ *     section 3.2.3, the ITC form that marks existing tokens as global);
+ *   - the key blocks listed for (h, block of i) in block_layout: BigBird's random and sliding
+ *     blocks (Big Bird notes, sections 3.2.2 and 3.3).
+ * Padded keys are never attended (Longformer hub page, section 5: a 0 in the attention mask
+ * marks padding).  A query row whose set is empty gets out = 0 and lse = -inf.
+ *
+ * Layout.  q, k, v, out: contiguous [batch][heads][n][d] (row-major, "BHND"), all of `dtype`.
+ * lse: contiguous fp32 [batch][heads][n].  bf16 values are stored as raw 16-bit patterns.
+ *
+ * Ownership.  Every tensor pointer is DEVICE memory allocated and owned by the caller, except
+ * `dilation`, which is a HOST array read during the call.  The library allocates no device
+ * memory and keeps no state between calls; scratch space comes from the caller's workspace.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream): results are
+ * valid once the stream has been synchronised.  Concurrent calls on different streams must
+ * use different workspaces.
+ *
+ * Errors.  A call that returns anything but LONGATTN_OK has launched nothing (except
+ * LONGATTN_ERR_HIP, which reports a failed launch).  No exception crosses this interface.
+ * With the environment variable LONGATTN_DEBUG=1 the library also copies global_idx and
+ * block_layout to the host and checks their contents (sorted, distinct, in range).
+ */
+#ifndef LONGATTN_H
+#define LONGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum longattn_status {
+  LONGATTN_OK = 0,
+  LONGATTN_ERR_INVALID_ARG = 1, /* a size, window, dilation, index or pointer is out of range */
+  LONGATTN_ERR_UNSUPPORTED = 2, /* valid, but this build has no kernel for it (see below)     */
+  LONGATTN_ERR_ALIGNMENT = 3,   /* q, k, v or out is not 16-byte aligned                       */
+  LONGATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than longattn_workspace_size  */
+  LONGATTN_ERR_HIP = 5          /* the HIP runtime reported an error while launching           */
+} longattn_status;
+
+typedef enum longattn_dtype { LONGATTN_BF16 = 0, LONGATTN_F32 = 1 } longattn_dtype;
+
+typedef struct longattn_desc {
+  int32_t batch, heads, n, d; /* each >= 0; d >= 1                                             */
+  int32_t dtype;              /* longattn_dtype of q, k, v and out                             */
+  float scale;                /* > 0 and finite; 1/sqrt(d) for standard attention            */
+  int32_t win_left;           /* one-sided inclusive extents in dilated steps, >= 0;          */
+  int32_t win_right;          /*   win_left = win_right = -1 switches the window off          */
+  const int32_t* dilation;    /* HOST [heads], each >= 1; NULL = 1 for every head              */
+  const int32_t* global_idx;  /* DEVICE [batch][n_global]: per sample ascending, distinct,
+                                 each in [0, n)                                               */
+  int32_t n_global;           /* 0 = no global tokens; n_global <= n                           */
+  const uint8_t* key_pad;     /* DEVICE [batch][n], nonzero = padded key; NULL = no padding    */
+  const int32_t* block_layout; /* DEVICE [heads][n/block][max_kb] key-block ids, distinct per
+                                  row, -1 = unused slot; NULL = no block layout               */
+  int32_t block;              /* layout block size: n % block == 0                             */
+  int32_t max_kb;             /* slots per layout row                                          */
+} longattn_desc;
+
+/*
+ * What the GPU kernels implement (anything else valid returns LONGATTN_ERR_UNSUPPORTED):
+ *   bf16: d in {64, 128}; either the window or the block layout (not both at once); layout
+ *         block in {64, 128}; dilation <= 255 and, if the heads' dilations differ, heads <= 256.
+ *   fp32: 1 <= d <= 256; every combination of window, dilation, globals, padding and layout.
+ */
+
+/* Bytes of device workspace longattn_forward needs for this descriptor (0 if none).
+ * The answer depends only on the descriptor's sizes and dtype. */
+longattn_status longattn_workspace_size(const longattn_desc* desc, size_t* bytes);
+
+/* One forward pass.  q, k, v: DEVICE [B][H][n][d] inputs; out: DEVICE [B][H][n][d] output;
+ * lse: DEVICE fp32 [B][H][n] output or NULL; workspace: DEVICE scratch of at least
+ * longattn_workspace_size bytes (may be NULL when that size is 0). */
+longattn_status longattn_forward(const longattn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The same pass, recording caller-created hipEvent_t handles on `stream` at its phase
+ * boundaries so the caller can time each kernel: marks[0] before the main sparse kernel,
+ * marks[1] after it, marks[2] after the global-row partial kernel, marks[3] after the
+ * global-row combine kernel (phases that do not run leave consecutive marks equal).
+ * n_marks must be 0 (no marks, same as longattn_forward) or LONGATTN_N_MARKS. */
+#define LONGATTN_N_MARKS 4
+longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
+                                        const void* v, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        void* const* marks, int32_t n_marks);
+
+/* Useful score entries, counted on the GPU: entries_out is a DEVICE int64[2] that receives
+ * [0] E = sum over all (b, h, i) of |S(b, h, i)| and [1] the part of E in global-token rows
+ * (asynchronous on `stream`).  4 * d * E is the useful floating-point work of one forward pass
+ * (2d for the score dot product and 2d for the weighted value sum of each entry). */
+longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entries_out,
+                                       void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* longattn_status_string(longattn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGATTN_H */

@@ -1,0 +1,279 @@
+"""Banded sparse self-attention forward for AMD MI355X (gfx950): Python binding.
+
+This module only marshals arguments for ``liblongattn.so`` (built from ``csrc/`` by
+``python -m sparse_long_sequence_banded_amd.build``); every step of the attention runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current HIP stream.  If the
+library has not been built, every call raises ``LongAttnNotBuilt``; there is no fallback.
+
+The C entry points keep their names here (``longattn_forward``, ``longattn_workspace_size``,
+``longattn_forward_marked``, ``longattn_count_entries``, ``longattn_status_string``); the
+``forward`` / ``count_entries`` helpers wrap them for torch tensors.
+"""
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblongattn.so")
+
+LONGATTN_OK = 0
+LONGATTN_ERR_INVALID_ARG = 1
+LONGATTN_ERR_UNSUPPORTED = 2
+LONGATTN_ERR_ALIGNMENT = 3
+LONGATTN_ERR_WORKSPACE = 4
+LONGATTN_ERR_HIP = 5
+LONGATTN_BF16 = 0
+LONGATTN_F32 = 1
+LONGATTN_N_MARKS = 4
+
+EXPORTED = (
+    "longattn_workspace_size",
+    "longattn_forward",
+    "longattn_forward_marked",
+    "longattn_count_entries",
+    "longattn_status_string",
+)
+
+
+class longattn_desc(ctypes.Structure):
+    """Mirror of ``struct longattn_desc`` in include/longattn.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("win_left", ctypes.c_int32),
+        ("win_right", ctypes.c_int32),
+        ("dilation", ctypes.c_void_p),
+        ("global_idx", ctypes.c_void_p),
+        ("n_global", ctypes.c_int32),
+        ("key_pad", ctypes.c_void_p),
+        ("block_layout", ctypes.c_void_p),
+        ("block", ctypes.c_int32),
+        ("max_kb", ctypes.c_int32),
+    ]
+
+
+class LongAttnNotBuilt(RuntimeError):
+    pass
+
+
+class LongAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {longattn_status_string(status)} (status {status})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load():
+    """Load liblongattn.so (raises LongAttnNotBuilt if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise LongAttnNotBuilt(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m sparse_long_sequence_banded_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            P = ctypes.c_void_p
+            D = ctypes.POINTER(longattn_desc)
+            lib.longattn_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+            lib.longattn_workspace_size.restype = ctypes.c_int
+            lib.longattn_forward.argtypes = [D, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.longattn_forward.restype = ctypes.c_int
+            lib.longattn_forward_marked.argtypes = [D, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                                    ctypes.POINTER(P), ctypes.c_int32]
+            lib.longattn_forward_marked.restype = ctypes.c_int
+            lib.longattn_count_entries.argtypes = [D, P, P]
+            lib.longattn_count_entries.restype = ctypes.c_int
+            lib.longattn_status_string.argtypes = [ctypes.c_int]
+            lib.longattn_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------------------------- raw C calls
+def longattn_status_string(status: int) -> str:
+    return load().longattn_status_string(int(status)).decode()
+
+
+def longattn_workspace_size(desc: longattn_desc) -> Tuple[int, int]:
+    """Returns (status, bytes)."""
+    nbytes = ctypes.c_size_t(0)
+    st = load().longattn_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes))
+    return st, int(nbytes.value)
+
+
+def longattn_forward(desc, q, k, v, out, lse, workspace, workspace_bytes, stream) -> int:
+    """Raw call; pointer arguments are integers (device addresses) or None."""
+    return load().longattn_forward(ctypes.byref(desc), q, k, v, out, lse, workspace,
+                                   int(workspace_bytes), stream)
+
+
+def longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes, stream,
+                            marks: Optional[Sequence[int]]) -> int:
+    arr = None
+    n = 0
+    if marks is not None:
+        n = len(marks)
+        arr = (ctypes.c_void_p * n)(*marks)
+    return load().longattn_forward_marked(ctypes.byref(desc), q, k, v, out, lse, workspace,
+                                          int(workspace_bytes), stream, arr, n)
+
+
+def longattn_count_entries(desc, entries_out, stream) -> int:
+    return load().longattn_count_entries(ctypes.byref(desc), entries_out, stream)
+
+
+# ----------------------------------------------------------------------------- torch helpers
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def make_desc(q, *, scale: Optional[float] = None, win_left: int = -1, win_right: int = -1,
+              dilation=None, global_idx=None, key_pad=None, block_layout=None, block: int = 0):
+    """Build the descriptor for q of shape [B, H, n, d].  Returns (desc, keepalive)."""
+    import torch
+
+    B, H, n, d = q.shape
+    if q.dtype == torch.bfloat16:
+        dt = LONGATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = LONGATTN_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+    keep = []
+    dil_ptr = None
+    if dilation is not None:
+        vals = [int(x) for x in dilation]
+        if len(vals) != H:
+            raise ValueError("dilation needs one entry per head")
+        dil = (ctypes.c_int32 * H)(*vals)
+        keep.append(dil)
+        dil_ptr = ctypes.cast(dil, ctypes.c_void_p).value
+    g = 0
+    if global_idx is not None:
+        if global_idx.dtype != torch.int32 or global_idx.device != q.device:
+            raise TypeError("global_idx must be an int32 tensor on q's device")
+        global_idx = global_idx.contiguous()
+        if global_idx.shape[0] != B:
+            raise ValueError("global_idx must be [batch, n_global]")
+        g = int(global_idx.shape[1])
+        keep.append(global_idx)
+    if key_pad is not None:
+        if key_pad.dtype not in (torch.uint8, torch.bool) or key_pad.device != q.device:
+            raise TypeError("key_pad must be a uint8/bool tensor on q's device")
+        key_pad = key_pad.contiguous().view(torch.uint8)
+        if tuple(key_pad.shape) != (B, n):
+            raise ValueError("key_pad must be [batch, n]")
+        keep.append(key_pad)
+    max_kb = 0
+    if block_layout is not None:
+        if block_layout.dtype != torch.int32 or block_layout.device != q.device:
+            raise TypeError("block_layout must be an int32 tensor on q's device")
+        block_layout = block_layout.contiguous()
+        max_kb = int(block_layout.shape[-1])
+        keep.append(block_layout)
+    desc = longattn_desc(
+        batch=B, heads=H, n=n, d=d, dtype=dt,
+        scale=float(scale) if scale is not None else 1.0 / float(d) ** 0.5,
+        win_left=int(win_left), win_right=int(win_right), dilation=dil_ptr,
+        global_idx=_ptr(global_idx), n_global=g, key_pad=_ptr(key_pad),
+        block_layout=_ptr(block_layout), block=int(block), max_kb=max_kb,
+    )
+    return desc, keep
+
+
+def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
+            win_right: int = -1, dilation=None, global_idx=None, key_pad=None,
+            block_layout=None, block: int = 0, out=None, lse=None, want_lse: bool = True,
+            workspace=None, stream=None, marks=None):
+    """Banded / global / block-sparse attention forward on torch device tensors [B, H, n, d].
+
+    Returns (out, lse); lse is None when ``want_lse`` is False and no ``lse`` is given.
+    """
+    import torch
+
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    desc, keep = make_desc(q, scale=scale, win_left=win_left, win_right=win_right,
+                           dilation=dilation, global_idx=global_idx, key_pad=key_pad,
+                           block_layout=block_layout, block=block)
+    st, ws_bytes = longattn_workspace_size(desc)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_workspace_size")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    sh = _stream_handle(stream)
+    if marks is None:
+        st = longattn_forward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              _ptr(lse), _ptr(workspace) if ws_bytes else None, ws_bytes, sh)
+    else:
+        st = longattn_forward_marked(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     out.data_ptr(), _ptr(lse),
+                                     _ptr(workspace) if ws_bytes else None, ws_bytes, sh, marks)
+    del keep
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_forward")
+    return out, lse
+
+
+def count_entries(q, *, win_left: int = -1, win_right: int = -1, dilation=None,
+                  global_idx=None, key_pad=None, block_layout=None, block: int = 0,
+                  stream=None) -> Tuple[int, int]:
+    """(E, E in global rows): useful score entries counted on the GPU (synchronises)."""
+    import torch
+
+    desc, keep = make_desc(q, win_left=win_left, win_right=win_right, dilation=dilation,
+                           global_idx=global_idx, key_pad=key_pad, block_layout=block_layout,
+                           block=block)
+    e = torch.zeros(2, dtype=torch.int64, device=q.device)
+    st = longattn_count_entries(desc, e.data_ptr(), _stream_handle(stream))
+    del keep
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_count_entries")
+    vals = e.cpu().tolist()
+    return int(vals[0]), int(vals[1])
+
+
+def from_hf_mask(mask):
+    """HF-style attention mask [B, n] with 0 = padding, 1 = local, 2 = global tokens
+    (Longformer hub page, section 5) -> (global_idx int32 [B, g], key_pad uint8 [B, n]).
+
+    Every sample must have the same number g of global tokens.
+    """
+    import torch
+
+    if mask.dim() != 2:
+        raise ValueError("mask must be [batch, n]")
+    is_g = mask == 2
+    counts = is_g.sum(dim=1)
+    if counts.numel() and not bool((counts == counts[0]).all()):
+        raise ValueError("every sample needs the same number of global tokens")
+    B = mask.shape[0]
+    g = int(counts[0]) if B else 0
+    idx = torch.nonzero(is_g, as_tuple=False)[:, 1].to(torch.int32).reshape(B, g)
+    key_pad = (mask == 0).to(torch.uint8)
+    return idx.contiguous(), key_pad.contiguous()

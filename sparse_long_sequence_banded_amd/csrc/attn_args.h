@@ -1,0 +1,46 @@
+// Internal launch arguments shared by the host dispatcher and the kernels (not public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace longattn {
+
+constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
+constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
+constexpr int kGlobalChunk = 512;     // keys per workgroup in the global-row partial kernel
+
+enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };
+
+// Passed by value to every kernel (kernarg segment, read through scalar loads).
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;
+  const int32_t* gidx;    // [B][g] or null
+  const uint8_t* kpad;    // [B][n] or null
+  const int32_t* layout;  // [H][n/block][max_kb] or null
+  float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
+  int B, H, n, g;
+  int wl, wr;             // window extents clamped to n; band_on == 0 means no window
+  int band_on;
+  int block, max_kb;
+  int chunks;             // key chunks of the global-row partial kernel
+  float scale;            // softmax scale (> 0)
+  float scale_log2;       // scale * log2(e)
+  int tiles_per_b;        // main-kernel workgroups per batch sample
+  int uniform_dil;        // > 0: every head has this dilation, tiles_per_head = tile_off[1]
+  int tile_off[kMaxTableHeads + 1];  // prefix sums of workgroups per head (non-uniform case)
+  uint8_t dil[kMaxTableHeads];
+};
+
+// Launchers (defined next to their kernels).
+hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s);
+hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, int nw, hipStream_t s);
+hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);
+
+}  // namespace longattn

@@ -1,0 +1,299 @@
+// C-ABI boundary: argument validation, planning and kernel dispatch.
+//
+// Nothing here computes attention; every arithmetic step runs in the kernels of attn_mfma.hip
+// (bf16) and attn_rowwise.hip (fp32 and the entry counter).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "attn_args.h"
+#include "longattn.h"
+
+using namespace longattn;
+
+namespace {
+
+constexpr int kBandRowsPerWorkgroup = 128;  // 4 waves x 32 query rows
+constexpr long kMaxElems = 1L << 46;        // B*H*n*d bound for 64-bit offset arithmetic
+constexpr int kMaxN = 1 << 28;              // keeps every position and sentinel in int32
+
+struct Plan {
+  FwdArgs a;
+  bool bf16 = false;
+  int mode = kBand;
+  long grid_main = 0;
+  int nw_global = 0;
+  size_t ws_bytes = 0;
+  bool empty = false;
+};
+
+bool debug_enabled() {
+  const char* e = std::getenv("LONGATTN_DEBUG");
+  return e && e[0] == '1';
+}
+
+longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
+  if (!d) return LONGATTN_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->heads < 0 || d->n < 0 || d->d < 1) return LONGATTN_ERR_INVALID_ARG;
+  if (d->dtype != LONGATTN_BF16 && d->dtype != LONGATTN_F32) return LONGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return LONGATTN_ERR_INVALID_ARG;
+  const bool band_off = d->win_left == -1 && d->win_right == -1;
+  if (!band_off && (d->win_left < 0 || d->win_right < 0)) return LONGATTN_ERR_INVALID_ARG;
+  if (d->n_global < 0 || d->n_global > d->n) return LONGATTN_ERR_INVALID_ARG;
+  if (d->n_global > 0 && !d->global_idx) return LONGATTN_ERR_INVALID_ARG;
+  if (d->block_layout) {
+    if (d->block < 1 || d->max_kb < 0 || (d->n % d->block) != 0) return LONGATTN_ERR_INVALID_ARG;
+  }
+  if (d->dilation) {
+    for (int h = 0; h < d->heads; ++h)
+      if (d->dilation[h] < 1) return LONGATTN_ERR_INVALID_ARG;
+  }
+  if (d->n > kMaxN) return LONGATTN_ERR_UNSUPPORTED;
+  {
+    long e = 1;
+    const long dims[4] = {d->batch, d->heads, d->n, d->d};
+    for (long x : dims) {
+      if (x == 0) { e = 0; break; }
+      if (e > kMaxElems / x) return LONGATTN_ERR_UNSUPPORTED;
+      e *= x;
+    }
+  }
+
+  Plan& p = *P;
+  p = Plan();
+  FwdArgs& a = p.a;
+  std::memset(&a, 0, sizeof(a));
+  p.bf16 = d->dtype == LONGATTN_BF16;
+  const bool has_layout = d->block_layout != nullptr;
+
+  if (for_forward) {
+    if (p.bf16) {
+      if (d->d != 64 && d->d != 128) return LONGATTN_ERR_UNSUPPORTED;
+      if (has_layout && !band_off) return LONGATTN_ERR_UNSUPPORTED;
+      if (has_layout && ((d->block != 64 && d->block != 128) || d->max_kb > 256))
+        return LONGATTN_ERR_UNSUPPORTED;
+    } else if (d->d > 256) {
+      return LONGATTN_ERR_UNSUPPORTED;
+    }
+  }
+
+  a.B = d->batch;
+  a.H = d->heads;
+  a.n = d->n;
+  a.g = d->n_global;
+  a.band_on = band_off ? 0 : 1;
+  a.wl = band_off ? 0 : std::min(d->win_left, d->n);  // extents beyond n reach no further key
+  a.wr = band_off ? 0 : std::min(d->win_right, d->n);
+  a.block = has_layout ? d->block : 0;
+  a.max_kb = has_layout ? d->max_kb : 0;
+  a.scale = d->scale;
+  a.scale_log2 = d->scale * 1.44269504088896340736f;
+
+  // Dilation: one value for all heads, or a per-head table carried in the kernel arguments.
+  // Without a window the dilation changes nothing, so it is dropped.
+  bool uniform = true;
+  int dil0 = 1;
+  if (d->dilation && a.band_on && d->heads > 0) {
+    dil0 = d->dilation[0];
+    for (int h = 1; h < d->heads; ++h) uniform = uniform && d->dilation[h] == dil0;
+  }
+  if (!uniform) {
+    if (d->heads > kMaxTableHeads) return LONGATTN_ERR_UNSUPPORTED;
+    for (int h = 0; h < d->heads; ++h)
+      if (d->dilation[h] > 255) return LONGATTN_ERR_UNSUPPORTED;
+  }
+  a.uniform_dil = uniform ? dil0 : 0;
+  if (!uniform)
+    for (int h = 0; h < d->heads; ++h) a.dil[h] = (uint8_t)d->dilation[h];
+
+  p.empty = (a.B == 0 || a.H == 0 || a.n == 0);
+  if (p.empty) return LONGATTN_OK;
+
+  if (p.bf16 && for_forward) {
+    p.mode = has_layout ? kLayout : kBand;
+    auto tiles_of_head = [&](int dl) -> long {
+      if (p.mode == kLayout) return a.n / a.block;
+      long t = 0;
+      for (int r = 0; r < dl && r < a.n; ++r) {
+        const long n_r = (a.n - r + dl - 1) / dl;
+        t += (n_r + kBandRowsPerWorkgroup - 1) / kBandRowsPerWorkgroup;
+      }
+      return t;
+    };
+    long per_b = 0;
+    if (uniform) {
+      const long th = tiles_of_head(dil0);
+      a.tile_off[0] = 0;
+      a.tile_off[1] = (int)th;
+      per_b = th * a.H;
+    } else {
+      a.tile_off[0] = 0;
+      for (int h = 0; h < a.H; ++h) {
+        per_b += tiles_of_head(a.dil[h]);
+        a.tile_off[h + 1] = (int)per_b;
+      }
+    }
+    if (per_b * a.B > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+    a.tiles_per_b = (int)per_b;
+    p.grid_main = per_b * a.B;
+    if (a.g > 0) {
+      a.chunks = (a.n + kGlobalChunk - 1) / kGlobalChunk;
+      p.nw_global = a.g <= 32 ? 1 : (a.g <= 64 ? 2 : 4);
+      const long qt = 32L * p.nw_global;
+      const long grid_g = (long)a.B * a.H * ((a.g + qt - 1) / qt) * a.chunks;
+      if (grid_g > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
+        return LONGATTN_ERR_UNSUPPORTED;
+      p.ws_bytes = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2) * sizeof(float);
+    }
+  } else if (for_forward) {
+    if ((long)a.B * a.H * a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  }
+  return LONGATTN_OK;
+}
+
+// LONGATTN_DEBUG=1: check the device-side index contents on the host before launching.
+longattn_status debug_check(const longattn_desc* d, hipStream_t s) {
+  if (hipStreamSynchronize(s) != hipSuccess) return LONGATTN_ERR_HIP;
+  if (d->n_global > 0) {
+    std::vector<int32_t> g((size_t)d->batch * d->n_global);
+    if (hipMemcpy(g.data(), d->global_idx, g.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return LONGATTN_ERR_HIP;
+    for (int b = 0; b < d->batch; ++b)
+      for (int c = 0; c < d->n_global; ++c) {
+        const int32_t x = g[(size_t)b * d->n_global + c];
+        if (x < 0 || x >= d->n) return LONGATTN_ERR_INVALID_ARG;
+        if (c > 0 && x <= g[(size_t)b * d->n_global + c - 1]) return LONGATTN_ERR_INVALID_ARG;
+      }
+  }
+  if (d->block_layout && d->max_kb > 0) {
+    const int nb = d->n / d->block;
+    std::vector<int32_t> l((size_t)d->heads * nb * d->max_kb);
+    if (hipMemcpy(l.data(), d->block_layout, l.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return LONGATTN_ERR_HIP;
+    for (size_t r = 0; r < l.size() / d->max_kb; ++r) {
+      std::vector<int32_t> row(l.begin() + r * d->max_kb, l.begin() + (r + 1) * d->max_kb);
+      for (int32_t x : row)
+        if (x < -1 || x >= nb) return LONGATTN_ERR_INVALID_ARG;
+      std::sort(row.begin(), row.end());
+      for (size_t e = 1; e < row.size(); ++e)
+        if (row[e] >= 0 && row[e] == row[e - 1]) return LONGATTN_ERR_INVALID_ARG;
+    }
+  }
+  return LONGATTN_OK;
+}
+
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+longattn_status longattn_workspace_size(const longattn_desc* desc, size_t* bytes) {
+  if (!bytes) return LONGATTN_ERR_INVALID_ARG;
+  Plan p;
+  const longattn_status st = plan_call(desc, true, &p);
+  if (st != LONGATTN_OK) return st;
+  *bytes = p.ws_bytes;
+  return LONGATTN_OK;
+}
+
+longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
+                                        const void* v, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        void* const* marks, int32_t n_marks) {
+  if (n_marks != 0 && n_marks != LONGATTN_N_MARKS) return LONGATTN_ERR_INVALID_ARG;
+  if (n_marks && !marks) return LONGATTN_ERR_INVALID_ARG;
+  Plan p;
+  longattn_status st = plan_call(desc, true, &p);
+  if (st != LONGATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> bool {
+    return !n_marks || hipEventRecord(reinterpret_cast<hipEvent_t>(marks[i]), s) == hipSuccess;
+  };
+  if (p.empty) {
+    for (int i = 0; i < n_marks; ++i)
+      if (!mark(i)) return LONGATTN_ERR_HIP;
+    return LONGATTN_OK;
+  }
+  if (!q || !k || !v || !out) return LONGATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return LONGATTN_ERR_ALIGNMENT;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return LONGATTN_ERR_WORKSPACE;
+  if (debug_enabled()) {
+    st = debug_check(desc, s);
+    if (st != LONGATTN_OK) return st;
+  }
+
+  FwdArgs& a = p.a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.gidx = desc->n_global > 0 ? desc->global_idx : nullptr;
+  a.kpad = desc->key_pad;
+  a.layout = desc->block_layout;
+  a.part = static_cast<float*>(workspace);
+
+  hipError_t e = hipSuccess;
+  if (!mark(0)) return LONGATTN_ERR_HIP;
+  if (p.bf16) {
+    e = launch_mfma_main(a, desc->d, p.mode, (int)p.grid_main, s);
+    if (e != hipSuccess || !mark(1)) return LONGATTN_ERR_HIP;
+    if (a.g > 0) {
+      e = launch_mfma_global_partial(a, desc->d, p.nw_global, s);
+      if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
+      e = launch_global_combine(a, desc->d, s);
+      if (e != hipSuccess || !mark(3)) return LONGATTN_ERR_HIP;
+    } else if (!mark(2) || !mark(3)) {
+      return LONGATTN_ERR_HIP;
+    }
+  } else {
+    e = launch_rowwise_f32(a, desc->d, s);
+    if (e != hipSuccess || !mark(1) || !mark(2) || !mark(3)) return LONGATTN_ERR_HIP;
+  }
+  return LONGATTN_OK;
+}
+
+longattn_status longattn_forward(const longattn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes, stream,
+                                 nullptr, 0);
+}
+
+longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entries_out,
+                                       void* stream) {
+  if (!entries_out) return LONGATTN_ERR_INVALID_ARG;
+  Plan p;
+  const longattn_status st = plan_call(desc, false, &p);
+  if (st != LONGATTN_OK) return st;
+  FwdArgs& a = p.a;
+  a.gidx = desc->n_global > 0 ? desc->global_idx : nullptr;
+  a.kpad = desc->key_pad;
+  a.layout = desc->block_layout;
+  if (p.empty) {
+    a.B = a.H = a.n = 0;
+  }
+  const hipError_t e = launch_count_entries(a, entries_out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
+}
+
+const char* longattn_status_string(longattn_status status) {
+  switch (status) {
+    case LONGATTN_OK: return "ok";
+    case LONGATTN_ERR_INVALID_ARG: return "invalid argument";
+    case LONGATTN_ERR_UNSUPPORTED: return "unsupported by the GPU kernels";
+    case LONGATTN_ERR_ALIGNMENT: return "q, k, v or out not 16-byte aligned";
+    case LONGATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case LONGATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Every test here calls the C-ABI library through the Python binding and needs an MI355X.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_long_sequence_banded_amd as la
+from tests.gpu_helpers import compare, gpu_count, heads_subset, parity, run_gpu
+from workloads import make_inputs, random_case, round_to_bf16_bits, workload
+from workloads.torch_io import to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.load()
+    yield
+
+
+# ------------------------------------------------------------------------------ named workloads
+@pytest.mark.parametrize("name", ["tiny_f32", "longformer_base", "bigbird_itc"])
+def test_workload_full_parity(name):
+    _note(f"[parity] {name} (all rows)")
+    inp = make_inputs(workload(name))
+    max_abs, E = parity(inp, name)
+    _note(f"[parity] {name}: max-abs {max_abs:.3e}, E {E}")
+
+
+@pytest.mark.parametrize("name,heads", [("dilated_16k", [0, 3, 4, 15]),
+                                        ("swa512_causal_32k", [0, 9])])
+def test_workload_sampled_heads_parity(name, heads):
+    """Full-size launch; the oracle checks every row of a sample of heads, and every row of
+    every head must be a convex combination of value rows (each output coordinate inside the
+    range of the values)."""
+    _note(f"[parity] {name} full launch, oracle on heads {heads}")
+    inp = make_inputs(workload(name))
+    o, l, _ = run_gpu(inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    v = inp.f64("v")
+    assert np.all(o <= v.max(axis=2, keepdims=True) + 2e-2)
+    assert np.all(o >= v.min(axis=2, keepdims=True) - 2e-2)
+    sub = heads_subset(inp, heads)
+    ref_o, ref_l, _ = oracle.forward_inputs(sub)
+    max_abs = compare(sub, o[:, heads], l[:, heads], ref_o, ref_l, name)
+    _note(f"[parity] {name}: max-abs {max_abs:.3e} on heads {heads}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "longformer_base", "dilated_16k",
+                                  "swa512_causal_32k", "bigbird_itc"])
+def test_workload_entry_count_is_exact(name):
+    inp = make_inputs(workload(name))
+    assert gpu_count(inp) == oracle.count_inputs(inp)
+
+
+# ------------------------------------------------------------------------------ random sweep
+def _sweep_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    for t in range(36):
+        dtype = "bf16" if t % 4 else "f32"
+        d = int(rng.choice([64, 128])) if dtype == "bf16" else int(rng.choice([8, 64, 100, 128]))
+        layout = dtype == "f32" and rng.random() < 0.3 or (dtype == "bf16" and t % 6 == 5)
+        block = int(rng.choice([64, 128])) if layout else 0
+        n = int(rng.choice([1, 2, 63, 65, 127, 129, 200, 257, 384, 641, 1000]))
+        if layout:
+            n = block * int(rng.integers(1, 7))
+        H = int(rng.integers(1, 4))
+        band = (not layout) or dtype == "f32" and rng.random() < 0.5
+        wl = int(rng.choice([0, 1, 5, 31, 64, 100, 300, 5000])) if band else -1
+        wr = int(rng.choice([0, 0, 3, 33, 63, 128, 200])) if band else -1
+        dil = [int(x) for x in rng.integers(1, 4, size=H)] if band and rng.random() < 0.5 else None
+        g = int(rng.integers(0, min(n, 70) + 1)) if rng.random() < 0.6 else 0
+        pad = str(rng.choice(["none", "tail", "random"]))
+        pc = int(rng.integers(0, n + 1))
+        cases.append(dict(seed=5000 + t, batch=int(rng.integers(1, 3)), heads=H, n=n, d=d,
+                          dtype=dtype, win_left=wl, win_right=wr, dilations=dil, n_global=g,
+                          pad=pad, pad_count=pc, block=block,
+                          max_kb=int(rng.integers(1, 5)) if layout else 0))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"s{i}" for i in range(len(SWEEP))])
+def test_random_shapes_parity(case):
+    _note(f"[sweep] {case}")
+    inp = random_case(**case)
+    parity(inp, str(case))
+    assert gpu_count(inp) == oracle.count_inputs(inp)
+
+
+# ------------------------------------------------------------------------------ edge cases
+def test_window_zero_returns_v_bits_exactly():
+    inp = random_case(31, batch=2, heads=3, n=300, d=64, win_left=0, win_right=0,
+                      dilations=[1, 2, 3])
+    _, _, out = run_gpu(inp)
+    bits = out.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, inp.v)
+
+
+def test_window_covering_sequence_is_full_attention():
+    n = 333
+    inp = random_case(32, batch=1, heads=2, n=n, d=128, win_left=n, win_right=n)
+    parity(inp, "full")
+
+
+def test_rows_whose_keys_are_all_padded_are_empty():
+    inp = random_case(33, batch=2, heads=2, n=256, d=64, win_left=3, win_right=3, n_global=2)
+    kp = np.zeros((2, 256), np.uint8)
+    kp[1, :] = 1  # sample 2: every key padded, so every row (global rows too) is empty
+    kp[0, 100:140] = 1  # sample 1: rows 104..135 see only padded window keys (plus globals)
+    inp.key_pad = kp
+    ref_o, ref_l, _ = oracle.forward_inputs(inp)
+    o, l, _ = run_gpu(inp)
+    compare(inp, o, l, ref_o, ref_l, "padded")
+    assert np.all(o[1] == 0.0) and np.all(l[1] == -np.inf)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_keys_contribute_exactly_zero(dtype):
+    """Padded keys poisoned with a huge finite value leave the output bit-identical."""
+    inp = random_case(34, batch=2, heads=2, n=520, d=64, dtype=dtype, win_left=40, win_right=7,
+                      dilations=[1, 2], n_global=5, pad="random", pad_count=60)
+    _, _, out_a = run_gpu(inp)
+    poisoned = random_case(34, batch=2, heads=2, n=520, d=64, dtype=dtype, win_left=40,
+                           win_right=7, dilations=[1, 2], n_global=5, pad="random", pad_count=60)
+    big = round_to_bf16_bits(np.array([1e30], np.float32))[0] if dtype == "bf16" else np.float32(1e30)
+    for b in range(2):
+        idx = np.nonzero(poisoned.key_pad[b])[0]
+        poisoned.k[b][:, idx] = big
+        poisoned.v[b][:, idx] = big
+    _, _, out_b = run_gpu(poisoned)
+    assert (out_a.cpu() == out_b.cpu()).all()
+
+
+def test_results_are_deterministic():
+    inp = make_inputs(workload("longformer_base"))
+    _, _, a = run_gpu(inp)
+    _, _, b = run_gpu(inp)
+    assert (a.cpu().view(__import__("torch").int16) == b.cpu().view(__import__("torch").int16)).all()
+
+
+def test_causal_window_with_global_tokens():
+    inp = random_case(35, batch=1, heads=2, n=1500, d=128, win_left=200, win_right=0,
+                      n_global=9)
+    parity(inp, "causal+globals")
+
+
+def test_global_tokens_only():
+    inp = random_case(36, batch=2, heads=2, n=700, d=64, n_global=40, pad="tail", pad_count=50)
+    parity(inp, "globals only")
+
+
+def test_uniform_and_per_head_dilation_tables():
+    for dil in (3, [1, 2, 3, 4, 5]):
+        inp = random_case(37, batch=1, heads=5, n=900, d=64, win_left=17, win_right=9,
+                          dilations=dil, n_global=3)
+        parity(inp, f"dilation {dil}")
+
+
+def test_debug_mode_rejects_unsorted_global_tokens():
+    import torch
+
+    inp = random_case(38, batch=1, heads=1, n=128, d=64, win_left=4, win_right=4, n_global=3)
+    t = to_torch(inp, "cuda:0")
+    bad = t["global_idx"].flip(1).contiguous()
+    os.environ["LONGATTN_DEBUG"] = "1"
+    try:
+        with pytest.raises(la.LongAttnError) as ei:
+            la.forward(t["q"], t["k"], t["v"], win_left=4, win_right=4, global_idx=bad)
+        assert ei.value.status == la.LONGATTN_ERR_INVALID_ARG
+        la.forward(t["q"], t["k"], t["v"], win_left=4, win_right=4, global_idx=t["global_idx"])
+    finally:
+        del os.environ["LONGATTN_DEBUG"]
+    torch.cuda.synchronize()
+
+
+def test_marks_time_each_phase():
+    import ctypes
+
+    import torch
+
+    inp = make_inputs(workload("longformer_base"))
+    t = to_torch(inp, "cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(la.LONGATTN_N_MARKS)]
+    for e in ev:  # make sure the underlying events exist before handing them to the library
+        e.record()
+    torch.cuda.synchronize()
+    handles = [ctypes.c_void_p(e.cuda_event).value for e in ev]
+    la.forward(t["q"], t["k"], t["v"], scale=inp.scale, win_left=256, win_right=256,
+               global_idx=t["global_idx"], key_pad=t["key_pad"], marks=handles)
+    torch.cuda.synchronize()
+    spans = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    assert all(s >= 0 for s in spans) and spans[0] > 0

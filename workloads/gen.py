@@ -73,17 +73,18 @@ class Inputs:
             return bf16_bits_to_f32(a)
         return a.astype(np.float32)
 
-    def head_slice(self, h0: int, h1: int) -> "Inputs":
-        """The same problem restricted to heads [h0, h1) (used to bound CPU work)."""
+    def select_heads(self, heads) -> "Inputs":
+        """The same problem restricted to the listed heads (dilation and layout follow)."""
+        hs = list(heads)
         return Inputs(
-            batch=self.batch, heads=h1 - h0, n=self.n, d=self.d, dtype=self.dtype,
-            q=np.ascontiguousarray(self.q[:, h0:h1]),
-            k=np.ascontiguousarray(self.k[:, h0:h1]),
-            v=np.ascontiguousarray(self.v[:, h0:h1]),
+            batch=self.batch, heads=len(hs), n=self.n, d=self.d, dtype=self.dtype,
+            q=np.ascontiguousarray(self.q[:, hs]),
+            k=np.ascontiguousarray(self.k[:, hs]),
+            v=np.ascontiguousarray(self.v[:, hs]),
             scale=self.scale, win_left=self.win_left, win_right=self.win_right,
-            dilation=None if self.dilation is None else self.dilation[h0:h1].copy(),
+            dilation=None if self.dilation is None else self.dilation[hs].copy(),
             global_idx=self.global_idx, key_pad=self.key_pad,
-            layout=None if self.layout is None else np.ascontiguousarray(self.layout[h0:h1]),
+            layout=None if self.layout is None else np.ascontiguousarray(self.layout[hs]),
             block=self.block, max_kb=self.max_kb,
         )
 
