@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step is one full forward pass (main sparse kernel, global-row partials, global-row combine)
+One step is one full forward pass (global-row partials, main sparse kernel, global-row combine)
 over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
 timed back to back between two device synchronisations.  Useful work is 4*d*E floating-point
 operations, E being the number of allowed (query, key) score entries counted by the library on
@@ -136,7 +136,7 @@ def main():
 
     spans = np.array([[marks[s][i].elapsed_time(marks[s][i + 1]) for i in range(3)]
                       for s in range(args.steps)])  # ms
-    main_ms, part_ms, comb_ms = (float(x) for x in spans.mean(axis=0))
+    part_ms, main_ms, comb_ms = (float(x) for x in spans.mean(axis=0))
     ms_per_step = elapsed * 1e3 / args.steps
     useful_flop = 4.0 * inp.d * E
     value = useful_flop / (ms_per_step * 1e-3) / 1e12

@@ -78,7 +78,8 @@ typedef struct longattn_desc {
 /*
  * What the GPU kernels implement (anything else valid returns LONGATTN_ERR_UNSUPPORTED):
  *   bf16: d in {64, 128}; either the window or the block layout (not both at once); layout
- *         block in {64, 128}; dilation <= 255 and, if the heads' dilations differ, heads <= 256.
+ *         block in {64, 128}, max_kb <= 256; n_global <= 256; dilation <= 255 and, if the
+ *         heads' dilations differ, heads <= 256.
  *   fp32: 1 <= d <= 256; every combination of window, dilation, globals, padding and layout.
  */
 
@@ -94,9 +95,9 @@ longattn_status longattn_forward(const longattn_desc* desc, const void* q, const
                                  size_t workspace_bytes, void* stream);
 
 /* The same pass, recording caller-created hipEvent_t handles on `stream` at its phase
- * boundaries so the caller can time each kernel: marks[0] before the main sparse kernel,
- * marks[1] after it, marks[2] after the global-row partial kernel, marks[3] after the
- * global-row combine kernel (phases that do not run leave consecutive marks equal).
+ * boundaries so the caller can time each kernel: marks[0] before the first kernel, marks[1]
+ * after the global-row partial kernel, marks[2] after the main sparse kernel, marks[3] after
+ * the global-row combine kernel (phases that do not run leave consecutive marks equal).
  * n_marks must be 0 (no marks, same as longattn_forward) or LONGATTN_N_MARKS. */
 #define LONGATTN_N_MARKS 4
 longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,

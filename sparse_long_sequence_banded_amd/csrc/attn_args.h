@@ -9,6 +9,7 @@ namespace longattn {
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
 constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
 constexpr int kGlobalChunk = 512;     // keys per workgroup in the global-row partial kernel
+constexpr int kGlobalCap = 256;       // global tokens the bf16 kernels stage in LDS
 
 enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };
 
@@ -23,6 +24,7 @@ struct FwdArgs {
   const uint8_t* kpad;    // [B][n] or null
   const int32_t* layout;  // [H][n/block][max_kb] or null
   float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
+  int32_t* gmeta;         // [B][g]: global column position | (usable key) << 31
   int B, H, n, g;
   int wl, wr;             // window extents clamped to n; band_on == 0 means no window
   int band_on;
@@ -37,8 +39,10 @@ struct FwdArgs {
 };
 
 // Launchers (defined next to their kernels).
+int main_rows_per_workgroup(int mode, int block);
+int global_rows_per_workgroup(int g);
 hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s);
-hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, int nw, hipStream_t s);
+hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);

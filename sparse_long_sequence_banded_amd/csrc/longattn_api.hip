@@ -18,7 +18,6 @@ using namespace longattn;
 
 namespace {
 
-constexpr int kBandRowsPerWorkgroup = 128;  // 4 waves x 32 query rows
 constexpr long kMaxElems = 1L << 46;        // B*H*n*d bound for 64-bit offset arithmetic
 constexpr int kMaxN = 1 << 28;              // keeps every position and sentinel in int32
 
@@ -27,7 +26,7 @@ struct Plan {
   bool bf16 = false;
   int mode = kBand;
   long grid_main = 0;
-  int nw_global = 0;
+  size_t part_floats = 0;
   size_t ws_bytes = 0;
   bool empty = false;
 };
@@ -77,6 +76,7 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
       if (has_layout && !band_off) return LONGATTN_ERR_UNSUPPORTED;
       if (has_layout && ((d->block != 64 && d->block != 128) || d->max_kb > 256))
         return LONGATTN_ERR_UNSUPPORTED;
+      if (d->n_global > kGlobalCap) return LONGATTN_ERR_UNSUPPORTED;
     } else if (d->d > 256) {
       return LONGATTN_ERR_UNSUPPORTED;
     }
@@ -116,12 +116,13 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
 
   if (p.bf16 && for_forward) {
     p.mode = has_layout ? kLayout : kBand;
+    const int qt = main_rows_per_workgroup(p.mode, a.block);
     auto tiles_of_head = [&](int dl) -> long {
       if (p.mode == kLayout) return a.n / a.block;
       long t = 0;
       for (int r = 0; r < dl && r < a.n; ++r) {
         const long n_r = (a.n - r + dl - 1) / dl;
-        t += (n_r + kBandRowsPerWorkgroup - 1) / kBandRowsPerWorkgroup;
+        t += (n_r + qt - 1) / qt;
       }
       return t;
     };
@@ -143,12 +144,13 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
     p.grid_main = per_b * a.B;
     if (a.g > 0) {
       a.chunks = (a.n + kGlobalChunk - 1) / kGlobalChunk;
-      p.nw_global = a.g <= 32 ? 1 : (a.g <= 64 ? 2 : 4);
-      const long qt = 32L * p.nw_global;
-      const long grid_g = (long)a.B * a.H * ((a.g + qt - 1) / qt) * a.chunks;
+      const long gq = global_rows_per_workgroup(a.g);
+      const long grid_g = (long)a.B * a.H * ((a.g + gq - 1) / gq) * a.chunks;
       if (grid_g > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
         return LONGATTN_ERR_UNSUPPORTED;
-      p.ws_bytes = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2) * sizeof(float);
+      // partials (o, then m and l) followed by one int32 record per (batch, global column)
+      p.part_floats = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2);
+      p.ws_bytes = p.part_floats * sizeof(float) + (size_t)a.B * a.g * sizeof(int32_t);
     }
   } else if (for_forward) {
     if ((long)a.B * a.H * a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
@@ -239,23 +241,24 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   a.kpad = desc->key_pad;
   a.layout = desc->block_layout;
   a.part = static_cast<float*>(workspace);
+  a.gmeta = p.ws_bytes ? reinterpret_cast<int32_t*>(a.part + p.part_floats) : nullptr;
 
+  // bf16: global-row partials first (they also publish the global columns' positions and
+  // validity), then the main sparse kernel, then the global-row combine, which overwrites the
+  // rows of global tokens that the main kernel also produced.
   hipError_t e = hipSuccess;
   if (!mark(0)) return LONGATTN_ERR_HIP;
   if (p.bf16) {
-    e = launch_mfma_main(a, desc->d, p.mode, (int)p.grid_main, s);
+    if (a.g > 0) e = launch_mfma_global_partial(a, desc->d, s);
     if (e != hipSuccess || !mark(1)) return LONGATTN_ERR_HIP;
-    if (a.g > 0) {
-      e = launch_mfma_global_partial(a, desc->d, p.nw_global, s);
-      if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
-      e = launch_global_combine(a, desc->d, s);
-      if (e != hipSuccess || !mark(3)) return LONGATTN_ERR_HIP;
-    } else if (!mark(2) || !mark(3)) {
-      return LONGATTN_ERR_HIP;
-    }
+    e = launch_mfma_main(a, desc->d, p.mode, (int)p.grid_main, s);
+    if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
+    if (a.g > 0) e = launch_global_combine(a, desc->d, s);
+    if (e != hipSuccess || !mark(3)) return LONGATTN_ERR_HIP;
   } else {
+    if (!mark(1)) return LONGATTN_ERR_HIP;
     e = launch_rowwise_f32(a, desc->d, s);
-    if (e != hipSuccess || !mark(1) || !mark(2) || !mark(3)) return LONGATTN_ERR_HIP;
+    if (e != hipSuccess || !mark(2) || !mark(3)) return LONGATTN_ERR_HIP;
   }
   return LONGATTN_OK;
 }

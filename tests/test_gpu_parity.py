@@ -208,4 +208,4 @@ def test_marks_time_each_phase():
                global_idx=t["global_idx"], key_pad=t["key_pad"], marks=handles)
     torch.cuda.synchronize()
     spans = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
-    assert all(s >= 0 for s in spans) and spans[0] > 0
+    assert all(s >= 0 for s in spans) and spans[0] > 0 and spans[1] > 0
