@@ -77,9 +77,9 @@ typedef struct longattn_desc {
 
 /*
  * What the GPU kernels implement (anything else valid returns LONGATTN_ERR_UNSUPPORTED):
- *   bf16: d in {64, 128}; either the window or the block layout (not both at once); layout
- *         block in {64, 128}, max_kb <= 256; n_global <= 256; dilation <= 255 and, if the
- *         heads' dilations differ, heads <= 256.
+ *   bf16: d in {64, 128}; n * d * 2 < 2^31 (one head's K or V under 2 GiB); either the window
+ *         or the block layout (not both at once); layout block in {64, 128}, max_kb <= 256;
+ *         n_global <= 256; if the heads' dilations differ, each is <= 255 and heads <= 256.
  *   fp32: 1 <= d <= 256; every combination of window, dilation, globals, padding and layout.
  */
 

@@ -39,7 +39,7 @@ struct FwdArgs {
 };
 
 // Launchers (defined next to their kernels).
-int main_rows_per_workgroup(int mode, int block);
+int main_rows_per_workgroup(int mode, int d, int block);
 int global_rows_per_workgroup(int g);
 hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s);
 hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, hipStream_t s);

@@ -14,7 +14,10 @@
 // over the residue classes i = p (mod dil) (the window skips tokens like a dilated convolution,
 // Longformer hub page, section 2), so every key tile here is a plain contiguous or strided band.
 // Global-key columns are concatenated after the local keys and share one online softmax with
-// them, as the LongT5 guide describes for its side keys (blocking-helpers paragraph).
+// them, as the LongT5 guide describes for its side keys (blocking-helpers paragraph).  A global
+// key is attended by every query through its column, so window tiles drop global keys (a
+// per-tile bit mask shared by the whole workgroup) and layout rows drop global columns that lie
+// in one of their blocks; each edge is counted once.
 //
 // Wave-level math (32x32x16 bf16 MFMA, fp32 accumulate).  A wave owns QB blocks of 32 query rows
 // and computes transposed score blocks S^T = K Q^T, so every lane holds the scores of one query
@@ -22,13 +25,12 @@
 // sum are in-lane reductions plus one exchange with lane ^ 32.  The output is kept transposed,
 // O^T += V^T P^T, so softmax rescale factors are per lane.
 //
-// Data movement.  K and V tiles go from memory straight into LDS with 16-byte direct loads (no
-// register staging), double-buffered, one barrier per tile.  K rows are read back as MFMA A
-// operands with 16-byte reads; V stays row-major and its transposed A operand is read with the
-// transposing 64-bit LDS read.  Both layouts XOR-swizzle 16-byte chunks by row so that the reads
-// of a wave hit distinct banks.
-
-#include <type_traits>
+// Data movement.  K and V tiles go from memory straight into LDS with 16-byte buffer loads (no
+// register staging; the buffer range check turns rows past the sequence end into zeros), two
+// stages each, one barrier per tile.  Half of the waves move K, the other half V.  K rows are
+// read back as MFMA A operands with 16-byte reads; V stays row-major and its transposed A operand
+// is read with the transposing 64-bit LDS read.  Both layouts XOR-swizzle 16-byte chunks by row
+// so that the reads of a wave hit distinct banks.
 
 #include "attn_args.h"
 
@@ -46,8 +48,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr int kJrNone = -(1 << 29);  // "this global key is not in the query's residue class"
-constexpr float kRescaleLog2 = 8.f;  // rescale only when the running max grows by > 2^8
+constexpr float kRescaleLog2 = 8.f;  // move the row's reference only when its max exceeds it by > 2^8
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -63,13 +64,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0; the other counters are left
-// at their maxima), then barrier.  The explicit wait is required: the workgroup fence inside
-// __syncthreads() only orders this wave's LDS stores and does not count the LDS writes of
-// direct loads, so the compiler may otherwise reach the barrier with those loads in flight.
-__device__ __forceinline__ void wait_loads_then_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0) expcnt(7) lgkmcnt(15)
-  __syncthreads();
+// s if bit `bit` of w is set, else ninf (which holds -inf): a sign-extended one-bit field
+// extract and a bitfield select.
+__device__ __forceinline__ float keep_if_bit(float s, uint32_t w, int bit, float ninf) {
+  const int sel = __builtin_amdgcn_sbfe((int)w, bit, 1);
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(sel), "v"(s), "v"(ninf));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(const void, p)));
 }
 
 // Logical workgroup id such that consecutive ids run on the same XCD.  Workgroups are handed to
@@ -97,12 +102,53 @@ __device__ __forceinline__ int swz_v(int row) {
 
 // Key tile descriptor, uniform over the workgroup.
 struct Tile {
-  int gathered;  // 0: row r at position base + stride * r; 1: global column base + r
+  int gathered;  // 0: row r at position base + kst * r (kst: the workgroup's key stride);
+                 // 1: row r is global column base + r
   int base;
-  int stride;
-  int count;     // rows >= count do not exist (their loads repeat a valid row; never attended)
+  int count;     // rows >= count do not exist (never attended; their loads return zeros or
+                 // repeat a valid row)
   int ks0;       // kBand window tiles: residue-subsequence index of row 0
 };
+
+// LDS stages of K tiles and of V tiles: two each (loads run one tile ahead).  At head dim 64 a
+// workgroup then needs about 34 KB of LDS, so four fit on a CU (more resident waves measured
+// faster than a third stage).
+template <int D>
+constexpr int kStages = 2;
+// Key-padding bits staged in LDS per workgroup: 64-bit words covering 4096 positions.
+constexpr int kPadWords = 64;
+
+// Wait until at most n of this wave's vector-memory loads are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, dword data format).  Loads at
+// offsets >= bytes return zeros.
+__device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte buffer load per lane straight into LDS: lane l's 16 bytes (from byte offset voff
+// of the resource) land at LDS byte address lds_base + 16*l.  Inline assembly so that the
+// compiler does not treat it as an LDS store it must order against LDS reads of other stages
+// (it would wait for every load in flight); the wave waits for these loads itself (vmcnt) before
+// the tile barrier.  No output registers; the operands are consumed when the load issues.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
 
 template <int D, int NW, int QB, int MODE>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
@@ -113,24 +159,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;         // MFMA k-steps over the head dim
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int MAT = kKeyTile * D * 2;
+  constexpr int NS = kStages<D>;
+  static_assert(NS == 2 || NS == 3, "stage count");
   constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
   constexpr int LPW = NLOAD / NW;    // of which each wave issues
   constexpr int RPB = 64 / CH;       // rows per 1 KB block
   constexpr int GREG = kGlobalCap / NT;
-  static_assert(NLOAD % NW == 0, "direct-load blocks must split evenly over the waves");
+  static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
   static_assert(kGlobalCap % NT == 0, "global staging must split evenly");
   constexpr bool kHasGlobalCols = MODE != kGlobalRows;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[2 * MAT];
-  __shared__ __attribute__((aligned(1024))) unsigned char st1[2 * MAT];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage_k[NS][MAT];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage_v[NS][MAT];
   __shared__ int lay_list[MODE == kLayout ? 256 : 1];
   __shared__ int lay_cnt;
   __shared__ __attribute__((aligned(16))) int g_pos[kHasGlobalCols ? kGlobalCap : 1];
-  __shared__ __attribute__((aligned(16))) int g_jr[kHasGlobalCols ? kGlobalCap : 1];
   __shared__ unsigned long long g_valid[kHasGlobalCols ? kGlobalCap / 64 : 1];
+  __shared__ unsigned long long g_bits[MODE == kBand ? kPadWords : 1];
+  __shared__ unsigned long long pad_bits[kPadWords];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int qj = lane & 31, hh = lane >> 5;
 
   // ------------------------------------------------------------------ work decomposition
@@ -176,6 +226,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       q0 = r * a.block;  // kLayout: query block r (QT == block)
     }
   }
+  // key stride of the local tiles (dilation of this head in window mode)
+  const int kst = (MODE == kBand) ? min(dl, a.n) : 1;
   const long bh = (long)b * a.H + h;
   const uint16_t* Qb = a.q + bh * a.n * D;
   const uint16_t* Kb = a.k + bh * a.n * D;
@@ -184,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int* gb = a.gidx ? a.gidx + (long)b * a.g : nullptr;
 
   // ------------------------------------------------------------------ query rows of this lane
-  // Lane (qj, hh) holds query qb*32 + qj of the wave for every query block qb.
+  // Lane (qj, hh) holds query row wave*RW + 32qb + qj of the workgroup for every block qb.
   int qpos[QB];  // sequence position, -1 = no such row
   int qsub[QB];  // kBand: residue-subsequence index
 #pragma unroll
@@ -205,6 +257,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       }
     }
   }
+  // Q fragments (B operands of the score MFMAs), loaded once.
+  const float c2 = a.scale_log2;
   u32x4 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -214,6 +268,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       if (qpos[qb] >= 0)
         qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
     }
+  // Consume the fragments here so that the compiler waits for these loads before the tile loop;
+  // otherwise it waits for them (vmcnt(0), which also drains the K/V prefetch) inside the loop.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
 
   // kGlobalRows also publishes, once per (batch, global column), the column's position and
   // whether it is a usable key (in range, not padded) for the main kernel.
@@ -225,7 +285,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         if (c < a.g) {
           const int x = gb[c];
           const bool ok = x >= 0 && x < a.n && !(pad && pad[x]);
-          a.gmeta[(long)b * a.g + c] = ok ? (int)(0x80000000u | (uint32_t)x) : 0;
+          const int xc = min(max(x, 0), a.n);  // keeps the records ascending
+          a.gmeta[(long)b * a.g + c] = (int)((ok ? 0x80000000u : 0u) | (uint32_t)xc);
         }
       }
     }
@@ -274,105 +335,154 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     if (t >= n_local) {
       T.gathered = 1;
       T.base = (t - n_local) * kKeyTile;
-      T.stride = 1;
       T.count = min(kKeyTile, a.g - T.base);
     } else if constexpr (MODE == kBand) {
       T.gathered = 0;
       T.ks0 = k_lo + t * kKeyTile;
       T.base = p + dl * T.ks0;
-      T.stride = dl;
       T.count = min(kKeyTile, np - T.ks0);
     } else if constexpr (MODE == kLayout) {
       T.gathered = 0;
       T.base = lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
-      T.stride = 1;
       T.count = kKeyTile;
     } else {
       T.gathered = 0;
       T.base = k_lo + t * kKeyTile;
-      T.stride = 1;
       T.count = min(kKeyTile, k_hi + 1 - T.base);
     }
     return T;
   };
 
-  // ------------------------------------------------------------------ global columns
-  // Positions, residue coordinates (for de-duplication against the window) and validity of
-  // the global-key columns, staged once per workgroup in LDS.  The per-column records are
-  // fetched at kernel start and written to LDS after the first tile's barrier.
-  int gm_reg[GREG];
+  // ------------------------------------------------------------------ staging in LDS
+  // Global-key columns: position and validity, once per workgroup.  A usable global key is
+  // attended through the global-column tiles by every query, so in window mode the local tiles
+  // drop it (each edge is counted once): g_bits marks the global keys among the window keys,
+  // bit i of word t for residue index k_lo + 64t + i, when the window range fits; otherwise
+  // each local tile searches the sorted positions.
+  const bool gbits_staged = MODE == kBand && n_gtiles > 0 && n_local <= kPadWords;
   if constexpr (kHasGlobalCols) {
-#pragma unroll
-    for (int i = 0; i < GREG; ++i) {
-      const int c = tid + NT * i;
-      gm_reg[i] = (n_gtiles > 0 && c < a.g) ? a.gmeta[(long)b * a.g + c] : 0;
-    }
-  }
-  auto stage_globals = [&]() {
-    if constexpr (kHasGlobalCols) {
+    if (n_gtiles > 0) {
+      if constexpr (MODE == kBand) {
+        if (gbits_staged) {
+          for (int w = tid; w < n_local; w += NT) g_bits[w] = 0ull;
+          __syncthreads();
+        }
+      }
 #pragma unroll
       for (int i = 0; i < GREG; ++i) {
         const int c = tid + NT * i;
-        const int m = gm_reg[i];
+        const int m = (c < a.g) ? a.gmeta[(long)b * a.g + c] : a.n;
         bool ok = c < a.g && m < 0;  // bit 31: usable key
         const int pos = m & 0x7fffffff;
         if constexpr (MODE == kLayout) {
+          // a global key inside one of this row's layout blocks is attended through the block
           const int blk = pos / a.block;
           for (int e = 0; e < lay_cnt; ++e) ok = ok && (lay_list[e] != blk);
         }
-        int jr = kJrNone;
         if constexpr (MODE == kBand) {
           const int rel = pos - p;
-          if (rel >= 0 && rel % dl == 0) jr = rel / dl;
+          if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
+            const int j = rel / dl - k_lo;
+            if (j >= 0 && j < kKeyTile * n_local) atomicOr(&g_bits[j >> 6], 1ull << (j & 63));
+          }
         }
         g_pos[c] = pos;
-        g_jr[c] = jr;
         const unsigned long long vm = __ballot(ok);
         if (lane == 0) g_valid[c >> 6] = vm;
       }
     }
-  };
+  }
+  // Key padding of the positions the local tiles can reach, as bits (bit i of word w: position
+  // pad_lo + 64w + i is a usable key), when they fit; otherwise each tile reads its pad bytes.
+  int pad_lo = 0;
+  bool pad_staged = false;
+  if (pad && n_local > 0) {
+    long lo, hi;
+    if constexpr (MODE == kBand) {
+      lo = p + (long)dl * k_lo;
+      hi = min((long)a.n - 1, p + (long)dl * (k_lo + (long)kKeyTile * n_local - 1));
+    } else if constexpr (MODE == kLayout) {
+      lo = 0;
+      hi = a.n - 1;
+    } else {
+      lo = k_lo;
+      hi = k_hi;
+    }
+    lo &= ~63L;
+    const long words = ((hi - lo) >> 6) + 1;
+    pad_staged = words <= kPadWords;
+    pad_lo = (int)lo;
+    if (pad_staged) {
+      for (int w = wave; w < (int)words; w += NW) {
+        const int pos = pad_lo + 64 * w + lane;
+        const bool ok = pos < a.n && pad[pos] == 0;
+        const unsigned long long m = __ballot(ok);
+        if (lane == 0) pad_bits[w] = m;
+      }
+    }
+  }
+  __syncthreads();
 
   // ------------------------------------------------------------------ tile loading
-  // Block j of this wave covers rows RPB*sub .. RPB*sub + RPB - 1 of matrix `mat`; lane l writes
-  // LDS bytes sub*1024 + 16*l, i.e. row RPB*sub + l/CH at swizzled chunk l%CH.
-  // Row of tile and element offset of the 16-byte chunk that this lane moves in block j (kept as
-  // a function of the lane, not in registers, to save VGPRs).
-  auto ld_row = [&](int j) -> int { return ((wave * LPW + j) % CH) * RPB + lane / CH; };
+  // Wave w moves the 1 KB blocks w*LPW .. w*LPW + LPW - 1 of a tile: all of one matrix (K for
+  // the first half of the waves, the "K waves", V for the rest).  Block `sub` of a matrix holds
+  // rows RPB*sub .. RPB*sub + RPB - 1; lane l moves row RPB*sub + l/CH, 16-byte chunk l%CH, to
+  // LDS byte sub*1024 + 16*l (the chunk's swizzled slot in that row).
+  const int mat = (wave * LPW) / CH;
+  const int sub0 = (wave * LPW) % CH;
+  auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
   auto ld_col = [&](int j) -> int {
-    const int blk = wave * LPW + j;
     const int row = ld_row(j);
-    return 8 * ((lane % CH) ^ (blk / CH == 0 ? swz_k<D>(row) : swz_v<D>(row)));
+    return 8 * ((lane % CH) ^ (mat == 0 ? swz_k<D>(row) : swz_v<D>(row)));
   };
+  // byte offsets of this lane's chunks within a local tile starting at row 0 (rows past the
+  // sequence end land at or beyond the resource size, so they read zeros)
+  uint32_t voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j)
+    voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
+  const uint16_t* msrc = (mat == 0) ? Kb : Vb;
   auto issue = [&](unsigned char* st, const Tile& T) {
-    int pos[LPW];
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + sub0 * 1024));
     if (kHasGlobalCols && T.gathered) {
+      const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) pos[j] = g_pos[T.base + min(ld_row(j), T.count - 1)];
+      for (int j = 0; j < LPW; ++j) {
+        const int pos = g_pos[T.base + min(ld_row(j), T.count - 1)];
+        lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
+      }
     } else {
+      const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) pos[j] = T.base + T.stride * min(ld_row(j), T.count - 1);
-    }
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = wave * LPW + j;
-      const int mat = blk / CH, sub = blk % CH;
-      const uint16_t* src = (mat == 0 ? Kb : Vb) + ((long)pos[j] * D + ld_col(j));
-      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, st + mat * MAT + sub * 1024), 16, 0, 0);
+      for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
     }
   };
-  // key validity of a local tile: in range and (if padding is given) not padded; the pad byte of
-  // row `lane` is loaded one tile ahead.  The load is issued on every path (from a harmless
-  // address when there is no padding or no such row) so that the register is only ever written
-  // by loads: overwriting it with a constant would force a wait for the loads in flight.
-  auto pad_byte = [&](const Tile& T) -> int {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(Kb);
-    if (pad && !T.gathered) src = pad + T.base + T.stride * min(lane, T.count - 1);
-    return *src;
+  // window mode: bits of the usable global keys among the rows of local tile t
+  auto global_keys = [&](const Tile& T, int t) -> unsigned long long {
+    if (n_gtiles == 0) return 0ull;
+    if (gbits_staged) return g_bits[t];
+    const bool in = lane < T.count;
+    const int pos = in ? T.base + kst * lane : 0;
+    int c = -1;  // last column with position <= pos (positions ascend)
+#pragma unroll
+    for (int step = kGlobalCap; step > 0; step >>= 1)
+      if (c + step < a.g && g_pos[c + step] <= pos) c += step;
+    const bool hit = in && c >= 0 && g_pos[c] == pos && ((g_valid[c >> 6] >> (c & 63)) & 1ull);
+    return __ballot(hit);
   };
-  auto local_valid = [&](const Tile& T, int pb) -> unsigned long long {
-    if (pad) return __ballot(lane < T.count && pb == 0);  // pb is a pad byte here
-    return T.count >= 64 ? ~0ull : ((1ull << T.count) - 1ull);
+  // allowed-key bits of a local tile (bit r: row r exists and is not padded)
+  auto local_valid = [&](const Tile& T) -> unsigned long long {
+    if (!pad) return T.count >= 64 ? ~0ull : ((1ull << T.count) - 1ull);
+    const bool in = lane < T.count;
+    const long pos = in ? (long)T.base + (long)kst * lane : 0;
+    bool ok;
+    if (pad_staged) {
+      const int rel = in ? (int)(pos - pad_lo) : 0;
+      ok = in && ((pad_bits[rel >> 6] >> (rel & 63)) & 1ull);
+    } else {
+      ok = in && pad[pos] == 0;
+    }
+    return __ballot(ok);
   };
 
   // ------------------------------------------------------------------ per-lane LDS read offsets
@@ -387,14 +497,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int vi = lane & 15, vg = lane >> 4;
   const int vrow0 = 4 * hh + (vi >> 2);
   const int vsw = swz_v<D>(vrow0);
-  int voff[DB];
+  int voffs[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int chunk = 4 * db + 2 * (vg & 1) + ((vi & 3) >> 1);
-    voff[db] = MAT + vrow0 * (2 * D) + ((chunk ^ vsw) * 16) + 8 * (vi & 1);
+    voffs[db] = vrow0 * (2 * D) + ((chunk ^ vsw) * 16) + 8 * (vi & 1);
   }
 
   // ------------------------------------------------------------------ running state
+  // Per row: ref = the exponent offset all weights of the row are taken against (log2 units),
+  // has = some allowed key has been seen, l = sum of the weights 2^(c2 s - ref), o = the weighted
+  // sum of value rows (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4).
   f32x16 o[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -402,13 +515,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-  float m_run[QB], l_run[QB];
+  float ref[QB], l_run[QB];
+  bool has[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = neg_inf();
+    ref[qb] = 0.f;
     l_run[qb] = 0.f;
+    has[qb] = false;
   }
-  const float c2 = a.scale_log2;
 
   // wave row range (kBand tile skipping)
   const int w_first = q0 + wave * RW;
@@ -419,209 +533,193 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   else wave_rows = (rg * QT + wave * RW) < a.g;
 
   // ------------------------------------------------------------------ one tile
-  // KIND 0: every key of the tile is allowed for every row of the wave (no masks);
-  // KIND 1: per-element masks from the key validity bits and, in window mode, the band edges;
-  // KIND 2: window mode global-key tile: validity bits plus removal of keys already attended
-  //         through the window.
-  // Each kind is compiled separately so the common interior tile carries no mask code.
-  const uint32_t span = (uint32_t)(a.wl + a.wr);
-  auto compute = [&](const unsigned char* st, const Tile& T, unsigned long long vmask,
-                     bool need_band, auto kind_c) {
-    constexpr int KIND = decltype(kind_c)::value;
-    // The 64-key tile is processed as two 32-key halves kb: scores of half kb for every query
-    // block, then the online-softmax step and the PV product of that half.  Keeping one half of
-    // scores live at a time halves their registers; the scores MFMAs of half 1 can run under
-    // the softmax VALU work of half 0.
+  // ---- raw scores S^T = K Q^T of both 32-key halves of a K tile, for every query block
+  auto scores = [&](const unsigned char* st, f32x16 (&sc)[2][QB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // ---- scores S^T = K Q^T for keys 32kb..32kb+31
-      f32x16 s[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(st + koff[ks] + kb * 32 * (2 * D));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb] = mfma_32x32x16(kf, qf[qb][ks], s[qb]);
+        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma_32x32x16(kf, qf[qb][ks], sc[kb][qb]);
       }
-
-      // ---- masks.  Register r holds key 32kb + 8(r/4) + 4hh + r%4, i.e. bit 8(r/4) + r%4 of
-      // w = (the tile's allowed keys for this lane's query) >> (32kb + 4hh).
-      if constexpr (KIND == 2) {
-        const uint32_t w = (uint32_t)(vmask >> (32 * kb + 4 * hh));
-        const int* jr = g_jr + T.base + 32 * kb;
+    }
+  };
+  // ---- masks, online softmax step and O^T += V^T P^T for one tile whose scores are in sc.
+  // Per-element masks (key validity bits and, in window mode, the band edges) are applied only
+  // when some key of the tile is excluded for some row of the wave; interior tiles skip them.
+  auto finish = [&](f32x16 (&sc)[2][QB], const unsigned char* st, const Tile& T,
+                    unsigned long long vmask, bool need_band) {
+    // ---- masks.  Register r of half kb holds key 32kb + 8(r/4) + 4hh + r%4, i.e. bit
+    // 8(r/4) + r%4 of w = (the tile's allowed keys for this lane's query) >> (32kb + 4hh).
+    if (need_band || vmask != ~0ull) {
+      const float ninf = neg_inf();
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const u32x4 jv = *reinterpret_cast<const u32x4*>(jr + 8 * g4 + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool ok = (w >> (8 * g4 + e)) & 1u;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              // a global key already inside this query's window is attended through the window
-              const bool dup = (uint32_t)((int)jv[e] - (qsub[qb] - a.wl)) <= span;
-              if (!ok || (a.band_on && dup)) s[qb][4 * g4 + e] = neg_inf();
-            }
+      for (int qb = 0; qb < QB; ++qb) {
+        unsigned long long m = vmask >> (4 * hh);
+        if (need_band) {
+          // keys k with qs - wl <= ks0 + k <= qs + wr, shifted by this lane's 4*hh
+          const int lo = qsub[qb] - a.wl - T.ks0 - 4 * hh;
+          const int hi = qsub[qb] + a.wr - T.ks0 - 4 * hh;
+          unsigned long long bm = 0ull;
+          if (hi >= 0 && lo <= 63) {
+            const int lc = max(lo, 0), hc = min(hi, 63);
+            bm = (~0ull >> (63 - (hc - lc))) << lc;
           }
+          m &= bm;
         }
-      } else if constexpr (KIND == 1) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          unsigned long long m = vmask >> (4 * hh);
-          if (need_band) {
-            // keys k with qs - wl <= ks0 + k <= qs + wr, shifted by this lane's 4*hh
-            const int lo = qsub[qb] - a.wl - T.ks0 - 4 * hh;
-            const int hi = qsub[qb] + a.wr - T.ks0 - 4 * hh;
-            unsigned long long bm = 0ull;
-            if (hi >= 0 && lo <= 63) {
-              const int lc = max(lo, 0), hc = min(hi, 63);
-              bm = (~0ull >> (63 - (hc - lc))) << lc;
-            }
-            m &= bm;
-          }
-          const uint32_t w = (uint32_t)(m >> (32 * kb));
+        for (int kb = 0; kb < 2; ++kb) {
+          uint32_t w = (uint32_t)(m >> (32 * kb));
+          asm("" : "+v"(w));  // per-lane word: the selects below stay two VALU ops each
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) s[qb][r] = neg_inf();
+            sc[kb][qb][r] = keep_if_bit(sc[kb][qb][r], w, 8 * (r >> 2) + (r & 3), ninf);
         }
       }
+    }
 
-      // ---- online softmax step in the log2 domain.  The running max is only raised when a
-      // row's maximum exceeds it by more than 2^8; until then the stale max keeps every weight
-      // below 2^8, which fp32 and bf16 hold without loss, and the final normalisation is exact.
-      float xm[QB];
-      bool need_any = false;
-      bool need[QB];
+    // ---- online softmax step over the 64 keys.  Weights are 2^(c2 s - ref), c2 = scale *
+    // log2(e).  ref only moves when a row sees its first allowed key (then ref := that tile's row
+    // max) or when a row's max exceeds ref by more than 2^8; otherwise every weight stays below
+    // 2^8, which fp32 and bf16 hold without loss, and the final normalisation by l makes the
+    // result exact.  In the common case no row moves: each weight is one FMA and one exp2.
+    float xm[QB];
+    bool need[QB];
+    bool need_any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const f32x16& u = sc[0][qb];
+      const f32x16& v = sc[1][qb];
+      float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
+      float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), u[15]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[0]), v[1]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[2]), v[3]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[4]), v[5]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[6]), v[7]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[8]), v[9]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[10]), v[11]);
+      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[12]), v[13]);
+      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[14]), __builtin_fmaxf(x1, v[15]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
+                                                       false, false);
+      const float x = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+      xm[qb] = x;
+      need[qb] = (x != neg_inf()) & (!has[qb] | (x - ref[qb] > kRescaleLog2));
+      need_any = need_any | need[qb];
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
+      // some row moves its reference (rare): per lane, the new reference is the row max if the
+      // row moves, else the old one
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const f32x16& sv = s[qb];
-        float x = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-        float y = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
-        x = fmaxf(fmaxf(x, sv[6]), sv[7]);
-        y = fmaxf(fmaxf(y, sv[8]), sv[9]);
-        x = fmaxf(fmaxf(x, sv[10]), sv[11]);
-        y = fmaxf(fmaxf(y, sv[12]), sv[13]);
-        x = fmaxf(fmaxf(x, sv[14]), fmaxf(y, sv[15]));
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                         false, false);
-        x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        xm[qb] = x;
-        need[qb] = x > m_run[qb] && (m_run[qb] == neg_inf() || (x - m_run[qb]) * c2 > kRescaleLog2);
-        need_any = need_any || need[qb];
+        const float nref = need[qb] ? xm[qb] : ref[qb];
+        const float alpha = has[qb] ? exp2_fast(ref[qb] - nref) : 1.f;  // old weights rescaled
+        ref[qb] = nref;
+        has[qb] = has[qb] || need[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
       }
-      if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float alpha = need[qb] ? exp2_fast((m_run[qb] - xm[qb]) * c2) : 1.f;
-          if (need[qb]) m_run[qb] = xm[qb];
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        }
-      }
+    }
 
 #pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t pk[QB][8];
+#pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const f32x16& sv = s[qb];
-        const float mc = (m_run[qb] == neg_inf()) ? 0.f : m_run[qb] * c2;
-        uint32_t pk[8];
+        const float nr = -ref[qb];
         float la = 0.f, lb = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-          const float p0 = exp2_fast(__builtin_fmaf(sv[r], c2, -mc));
-          const float p1 = exp2_fast(__builtin_fmaf(sv[r + 1], c2, -mc));
-          const float p2 = exp2_fast(__builtin_fmaf(sv[r + 2], c2, -mc));
-          const float p3 = exp2_fast(__builtin_fmaf(sv[r + 3], c2, -mc));
-          pk[r >> 1] = pack_bf16x2(p0, p1);
-          pk[(r >> 1) + 1] = pack_bf16x2(p2, p3);
+          const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 1], c2, nr));
+          const float p2 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 2], c2, nr));
+          const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
+          pk[qb][r >> 1] = pack_bf16x2(p0, p1);
+          pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
           la += p0 + p1;
           lb += p2 + p3;
         }
         l_run[qb] += la + lb;
-
-        // ---- O^T += V^T P^T for the two 16-key groups g = 2kb, 2kb+1 of this half
+      }
+      // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
 #pragma unroll
-        for (int gh = 0; gh < 2; ++gh) {
-          const int g = 2 * kb + gh;
-          const u32x4 bp = {pk[4 * gh + 0], pk[4 * gh + 1], pk[4 * gh + 2], pk[4 * gh + 3]};
+      for (int gh = 0; gh < 2; ++gh) {
+        const int g = 2 * kb + gh;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const unsigned char* vp = st + voff[db] + 16 * g * (2 * D);
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp));
-            const s16x4 v1 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp + 8 * (2 * D)));
-            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-            const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+        for (int db = 0; db < DB; ++db) {
+          const unsigned char* vp = st + voffs[db] + 16 * g * (2 * D);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp));
+          const s16x4 v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp + 8 * (2 * D)));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+          const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4 bp = {pk[qb][4 * gh + 0], pk[qb][4 * gh + 1], pk[qb][4 * gh + 2],
+                              pk[qb][4 * gh + 3]};
             o[qb][db] = mfma_32x32x16(va, bp, o[qb][db]);
           }
         }
       }
     }
   };
-  auto compute_tile = [&](const unsigned char* st, const Tile& T, unsigned long long vmask) {
-    bool need_band = false;
+  // Does tile T hold keys in reach of this wave's rows (window mode), and do band edges cut it?
+  auto reach = [&](const Tile& T, bool& need_band) -> bool {
+    need_band = false;
+    if (!wave_rows) return false;
     if constexpr (MODE == kBand) {
       if (!T.gathered) {
         const int kf = T.ks0, kl = T.ks0 + kKeyTile - 1;
-        if (kl < w_first - a.wl || kf > w_last + a.wr) return;  // no key of the tile in reach
+        if (kl < w_first - a.wl || kf > w_last + a.wr) return false;
         need_band = !(kf >= w_last - a.wl && kl <= w_first + a.wr);
       }
-      if (T.gathered) {
-        compute(st, T, vmask, false, std::integral_constant<int, 2>{});
-        return;
-      }
     }
-    if (need_band || vmask != ~0ull) compute(st, T, vmask, need_band, std::integral_constant<int, 1>{});
-    else compute(st, T, vmask, false, std::integral_constant<int, 0>{});
+    return true;
   };
 
   // ------------------------------------------------------------------ tile loop
-  // Two LDS stages: tile t computes from stage t%2 while tile t+1 streams into the other.  The
-  // barrier at the top of each step (it waits for this wave's outstanding loads first) makes
-  // tile t visible to every wave and retires every read of the stage about to be refilled.
+  // NS LDS stages of K tiles and NS of V tiles; tile t lives in stage t % NS while tiles
+  // t+1 .. t+NS-1 stream into the others.  At the top of step t each wave waits for its own
+  // loads of tile t (later tiles' loads stay in flight: loads complete in issue order), then the
+  // barrier makes tile t visible to every wave and retires every read of stage (t-1) % NS, which
+  // is refilled with tile t+NS-1 right after.
+  const bool kwave = mat == 0;
   if (n_tiles > 0) {
-    if (n_local == 0) {
-      stage_globals();
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
+    int st = 0;  // stage of tile t
+    for (int t = 0; t < n_tiles; ++t) {
+      if (NS == 3 && t + 1 < n_tiles) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
       __syncthreads();
-    }
-    int pb_next = 0;
-    {
-      const Tile T0 = tile_of(0);
-      issue(st0, T0);
-      pb_next = pad_byte(T0);
-    }
-    // One step: wait for tile t (this wave's loads, then the barrier for everyone's), start
-    // tile t+1 into the other stage, compute tile t.  The loop is unrolled by two so that the
-    // stage being read and the stage being filled are distinct arrays at compile time; with a
-    // run-time choice the compiler must assume they alias and would wait for the new loads
-    // before every LDS read.
-    auto step = [&](unsigned char* cur, unsigned char* nxt, int t) {
-      wait_loads_then_barrier();
+      const int stp = (st == 0) ? NS - 1 : st - 1;  // stage of tile t-1 (= that of t+NS-1)
+      if (t + NS - 1 < n_tiles) issue(kwave ? stage_k[stp] : stage_v[stp], tile_of(t + NS - 1));
       const Tile T = tile_of(t);
-      unsigned long long vmask;
-      if constexpr (kHasGlobalCols) {
-        vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T, pb_next);
-      } else {
-        vmask = local_valid(T, pb_next);
+      bool need_band = false;
+      if (reach(T, need_band)) {
+        unsigned long long vmask;
+        if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, t);
+        else if constexpr (kHasGlobalCols) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T);
+        else vmask = local_valid(T);
+        f32x16 sc[2][QB];
+        scores(stage_k[st], sc);
+        finish(sc, stage_v[st], T, vmask, need_band);
       }
-      if (t == 0 && n_local > 0 && n_gtiles > 0) {
-        stage_globals();
-        if (n_local == 1) __syncthreads();
-      }
-      if (t + 1 < n_tiles) {
-        const Tile Tn = tile_of(t + 1);
-        issue(nxt, Tn);
-        pb_next = pad_byte(Tn);
-      }
-      if (wave_rows) compute_tile(cur, T, vmask);
-    };
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(st0, st1, t);
-      if (t + 1 < n_tiles) step(st1, st0, t + 1);
+      st = (st + 1 == NS) ? 0 : st + 1;
     }
   }
 
@@ -629,28 +727,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(l_run[qb]), 32));
+    if (qpos[qb] < 0) continue;
     if constexpr (MODE == kGlobalRows) {
-      if (qpos[qb] >= 0) {
-        const int c = rg * QT + wave * RW + 32 * qb + qj;
-        const long slot = (bh * a.g + c) * a.chunks + ck;
-        float* po = a.part + slot * D;
+      const int c = rg * QT + wave * RW + 32 * qb + qj;
+      const long slot = (bh * a.g + c) * a.chunks + ck;
+      float* po = a.part + slot * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int d = 32 * db + 8 * rq + 4 * hh;
-            *reinterpret_cast<float4*>(po + d) =
-                make_float4(o[qb][db][4 * rq], o[qb][db][4 * rq + 1], o[qb][db][4 * rq + 2],
-                            o[qb][db][4 * rq + 3]);
-          }
-        if (hh == 0) {
-          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
-          pml[0] = (m_run[qb] == neg_inf()) ? neg_inf() : m_run[qb] * c2;
-          pml[1] = l_tot;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * hh;
+          *reinterpret_cast<float4*>(po + d) =
+              make_float4(o[qb][db][4 * rq], o[qb][db][4 * rq + 1], o[qb][db][4 * rq + 2],
+                          o[qb][db][4 * rq + 3]);
         }
+      if (hh == 0) {
+        float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
+        pml[0] = has[qb] ? ref[qb] : neg_inf();
+        pml[1] = l_tot;
       }
     } else {
-      if (qpos[qb] < 0) continue;
       const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
       uint16_t* orow = a.out + (bh * a.n + qpos[qb]) * D;
 #pragma unroll
@@ -665,56 +761,48 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
       if (a.lse && hh == 0)
         a.lse[bh * a.n + qpos[qb]] =
-            (l_tot > 0.f) ? (m_run[qb] * c2 + __log2f(l_tot)) * kLn2 : neg_inf();
+            (l_tot > 0.f) ? (ref[qb] + __log2f(l_tot)) * kLn2 : neg_inf();
     }
   }
 }
 
 // Merge the per-chunk partials of every global row and write its output and lse.
-// One wave per (batch, head, global row); each lane owns D/64 output columns.
+// One wave per (batch, head, global row), four rows per workgroup; lane l owns output columns
+// l, l + 64, ...  The (m, l) pairs of a row are the same for every lane of its wave (scalar
+// loads); the partial outputs of consecutive chunks are independent loads.
+constexpr int kCombineRows = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void global_combine_kernel(FwdArgs a) {
-  const int lane = threadIdx.x;
-  const long row = blockIdx.x;  // (b*H + h)*g + c
+__global__ __launch_bounds__(64 * kCombineRows) void global_combine_kernel(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long rows = (long)a.B * a.H * a.g;
+  const long row = (long)blockIdx.x * kCombineRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= rows) return;
   const long bh = row / a.g;
-  const int c = (int)(row % a.g);
+  const int c = (int)(row - bh * a.g);
   const int b = (int)(bh / a.H);
   const int pos = a.gidx[(long)b * a.g + c];
   if (pos < 0 || pos >= a.n) return;  // out-of-range global index: nothing to write
-  const float* po = a.part + row * a.chunks * D;
-  const float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + row * a.chunks * 2;
-  // each lane holds the (m, l) of chunks lane, lane + 64, ...
-  float M = -__builtin_inff();
-  for (int k = lane; k < a.chunks; k += 64) M = fmaxf(M, pml[2 * k]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const int K = a.chunks;
+  const float* po = a.part + row * K * D;
+  const float* pml = a.part + rows * K * D + row * K * 2;
+  constexpr float kNegInf = -__builtin_inff();
+  float M = kNegInf;
+  for (int k = 0; k < K; ++k) M = fmaxf(M, pml[2 * k]);
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float L = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int k0 = 0; k0 < a.chunks; k0 += 64) {
-      const int k = k0 + lane;
-      float w = 0.f, lk = 0.f;
-      if (k < a.chunks) {
-        const float mk = pml[2 * k];
-        if (mk != -__builtin_inff()) {
-          w = exp2f(mk - M);
-          lk = pml[2 * k + 1];
-        }
-      }
-      L += w * lk;
-      const int kn = min(64, a.chunks - k0);
-      for (int kk = 0; kk < kn; ++kk) {
-        const float wk = __shfl(w, kk);
-        if (wk == 0.f) continue;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int k = 0; k < K; ++k) {
+      const float mk = pml[2 * k];
+      const float w = (mk == kNegInf) ? 0.f : exp2f(mk - M);  // chunk's weights against M
+      L += w * pml[2 * k + 1];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += wk * po[(long)(k0 + kk) * D + lane + 64 * e];
-      }
+      for (int e = 0; e < PER; ++e) acc[e] += w * po[(long)k * D + lane + 64 * e];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
   uint16_t* orow = a.out + (bh * a.n + pos) * D;
@@ -724,7 +812,7 @@ __global__ __launch_bounds__(64) void global_combine_kernel(FwdArgs a) {
     orow[lane + 64 * e] = __builtin_bit_cast(uint16_t, (__bf16)v);
   }
   if (a.lse && lane == 0)
-    a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+    a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 template <int D, int NW, int QB, int MODE>
@@ -737,8 +825,12 @@ hipError_t launch_one(const FwdArgs& a, long grid, hipStream_t s) {
 
 }  // namespace
 
-// Query rows per workgroup of the main kernel: 128 in window mode, the block size in layout mode.
-int main_rows_per_workgroup(int mode, int block) { return mode == kLayout ? block : 128; }
+// Query rows per workgroup of the main kernel: 128 in window mode (four waves of one 32-row
+// block), the block size in layout mode.
+int main_rows_per_workgroup(int mode, int d, int block) {
+  (void)d;
+  return mode == kLayout ? block : 128;
+}
 
 hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s) {
   if (mode == kBand) {
@@ -749,7 +841,7 @@ hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStre
       if (d == 64) return launch_one<64, 2, 1, kLayout>(a, grid, s);
       if (d == 128) return launch_one<128, 2, 1, kLayout>(a, grid, s);
     } else if (a.block == 128) {
-      if (d == 64) return launch_one<64, 2, 2, kLayout>(a, grid, s);
+      if (d == 64) return launch_one<64, 4, 1, kLayout>(a, grid, s);
       if (d == 128) return launch_one<128, 4, 1, kLayout>(a, grid, s);
     }
   }
@@ -765,17 +857,18 @@ hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, hipStream_t s) {
     if (d == 64) return launch_one<64, 2, 1, kGlobalRows>(a, grid, s);
     if (d == 128) return launch_one<128, 2, 1, kGlobalRows>(a, grid, s);
   } else {
-    if (d == 64) return launch_one<64, 2, 2, kGlobalRows>(a, grid, s);
+    if (d == 64) return launch_one<64, 4, 1, kGlobalRows>(a, grid, s);
     if (d == 128) return launch_one<128, 4, 1, kGlobalRows>(a, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s) {
-  const long grid = (long)a.B * a.H * a.g;
-  if (grid <= 0) return hipSuccess;
-  if (d == 64) hipLaunchKernelGGL(global_combine_kernel<64>, dim3(grid), dim3(64), 0, s, a);
-  else if (d == 128) hipLaunchKernelGGL(global_combine_kernel<128>, dim3(grid), dim3(64), 0, s, a);
+  const long rows = (long)a.B * a.H * a.g;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + kCombineRows - 1) / kCombineRows)), block(64 * kCombineRows);
+  if (d == 64) hipLaunchKernelGGL(global_combine_kernel<64>, grid, block, 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL(global_combine_kernel<128>, grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -73,6 +73,8 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
   if (for_forward) {
     if (p.bf16) {
       if (d->d != 64 && d->d != 128) return LONGATTN_ERR_UNSUPPORTED;
+      // per-head K/V byte offsets are 32-bit buffer offsets in the kernels
+      if ((long)d->n * d->d * 2 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
       if (has_layout && !band_off) return LONGATTN_ERR_UNSUPPORTED;
       if (has_layout && ((d->block != 64 && d->block != 128) || d->max_kb > 256))
         return LONGATTN_ERR_UNSUPPORTED;
@@ -116,7 +118,7 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
 
   if (p.bf16 && for_forward) {
     p.mode = has_layout ? kLayout : kBand;
-    const int qt = main_rows_per_workgroup(p.mode, a.block);
+    const int qt = main_rows_per_workgroup(p.mode, d->d, a.block);
     auto tiles_of_head = [&](int dl) -> long {
       if (p.mode == kLayout) return a.n / a.block;
       long t = 0;
