@@ -95,11 +95,11 @@ longattn_status longattn_forward(const longattn_desc* desc, const void* q, const
                                  size_t workspace_bytes, void* stream);
 
 /* The same pass, recording caller-created hipEvent_t handles on `stream` at its phase
- * boundaries so the caller can time each kernel: marks[0] before the first kernel, marks[1]
- * after the global-row partial kernel, marks[2] after the main sparse kernel, marks[3] after
- * the global-row combine kernel (phases that do not run leave consecutive marks equal).
+ * boundaries so the caller can time each kernel: marks[0] before the attention kernel (every
+ * non-global row plus the global rows' per-chunk partials, one launch), marks[1] after it,
+ * marks[2] after the global-row combine kernel (equal to marks[1] when it does not run).
  * n_marks must be 0 (no marks, same as longattn_forward) or LONGATTN_N_MARKS. */
-#define LONGATTN_N_MARKS 4
+#define LONGATTN_N_MARKS 3
 longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
                                         const void* v, void* out, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream,

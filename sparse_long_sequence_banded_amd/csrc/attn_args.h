@@ -8,13 +8,13 @@ namespace longattn {
 
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
 constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
-constexpr int kGlobalChunk = 512;     // keys per workgroup in the global-row partial kernel
+constexpr int kGlobalChunk = 256;     // keys per global-row partial workgroup
 constexpr int kGlobalCap = 256;       // global tokens the bf16 kernels stage in LDS
 
 enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };
 
-// Passed by value to every kernel (kernarg segment, read through scalar loads).
-struct FwdArgs {
+// Scalar launch arguments.
+struct FwdCore {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -24,25 +24,29 @@ struct FwdArgs {
   const uint8_t* kpad;    // [B][n] or null
   const int32_t* layout;  // [H][n/block][max_kb] or null
   float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
-  int32_t* gmeta;         // [B][g]: global column position | (usable key) << 31
   int B, H, n, g;
   int wl, wr;             // window extents clamped to n; band_on == 0 means no window
   int band_on;
   int block, max_kb;
-  int chunks;             // key chunks of the global-row partial kernel
+  int chunks;             // key chunks of the global-row partial workgroups
+  int grid_rows;          // global-row partial workgroups in the attention launch
   float scale;            // softmax scale (> 0)
   float scale_log2;       // scale * log2(e)
   int tiles_per_b;        // main-kernel workgroups per batch sample
   int uniform_dil;        // > 0: every head has this dilation, tiles_per_head = tile_off[1]
+};
+
+// Passed by value to every kernel (kernarg segment, read through scalar loads).  Kernels that
+// hand the scalars to lambdas copy the FwdCore part into a local first: a lambda that captured
+// the whole argument by reference would make the compiler copy its tables to scratch memory.
+struct FwdArgs : FwdCore {
   int tile_off[kMaxTableHeads + 1];  // prefix sums of workgroups per head (non-uniform case)
   uint8_t dil[kMaxTableHeads];
 };
 
 // Launchers (defined next to their kernels).
 int main_rows_per_workgroup(int mode, int d, int block);
-int global_rows_per_workgroup(int g);
-hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s);
-hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s);
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);

@@ -32,6 +32,8 @@
 // is read with the transposing 64-bit LDS read.  Both layouts XOR-swizzle 16-byte chunks by row
 // so that the reads of a wave hit distinct banks.
 
+#include <type_traits>
+
 #include "attn_args.h"
 
 namespace longattn {
@@ -150,669 +152,732 @@ __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voff, uint
                : "memory", "m0");
 }
 
-template <int D, int NW, int QB, int MODE>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int RW = 32 * QB;        // query rows per wave
-  constexpr int QT = NW * RW;        // query rows per workgroup
-  constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int KS = D / 16;         // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int MAT = kKeyTile * D * 2;
-  constexpr int NS = kStages<D>;
-  static_assert(NS == 2 || NS == 3, "stage count");
-  constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
-  constexpr int LPW = NLOAD / NW;    // of which each wave issues
-  constexpr int RPB = 64 / CH;       // rows per 1 KB block
-  constexpr int GREG = kGlobalCap / NT;
-  static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
-  static_assert(kGlobalCap % NT == 0, "global staging must split evenly");
-  constexpr bool kHasGlobalCols = MODE != kGlobalRows;
+// LDS of one workgroup (either kind of work uses the same layout).
+template <int D>
+struct Smem {
+  __attribute__((aligned(1024))) unsigned char stage_k[kStages<D>][kKeyTile * D * 2];
+  __attribute__((aligned(1024))) unsigned char stage_v[kStages<D>][kKeyTile * D * 2];
+  int lay_list[256];                            // layout mode: valid key blocks of the row
+  __attribute__((aligned(16))) int g_pos[kGlobalCap];  // global columns: positions
+  unsigned long long g_valid[kGlobalCap / 64];  // global columns: usable-key bits
+  unsigned long long g_bits[kPadWords];         // window mode: global keys among window keys
+  unsigned long long pad_bits[kPadWords];       // key padding of the reachable positions
+  int lay_cnt;
+};
 
-  __shared__ __attribute__((aligned(1024))) unsigned char stage_k[NS][MAT];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage_v[NS][MAT];
-  __shared__ int lay_list[MODE == kLayout ? 256 : 1];
-  __shared__ int lay_cnt;
-  __shared__ __attribute__((aligned(16))) int g_pos[kHasGlobalCols ? kGlobalCap : 1];
-  __shared__ unsigned long long g_valid[kHasGlobalCols ? kGlobalCap / 64 : 1];
-  __shared__ unsigned long long g_bits[MODE == kBand ? kPadWords : 1];
-  __shared__ unsigned long long pad_bits[kPadWords];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int qj = lane & 31, hh = lane >> 5;
-
-  // ------------------------------------------------------------------ work decomposition
-  int b = 0, h = 0, dl = 1, p = 0, np = a.n, q0 = 0, ck = 0, rg = 0;
-  if constexpr (MODE == kGlobalRows) {
-    const int rgs = (a.g + QT - 1) / QT;
-    int x = blockIdx.x;
-    ck = x % a.chunks;
-    x /= a.chunks;
-    rg = x % rgs;
-    x /= rgs;
-    h = x % a.H;
-    b = x / a.H;
+// One launch runs the main workgroups (MODE_MAIN) and the global-row partial workgroups
+// together, so the latency-bound global-row chunks overlap the main work.  Logical ids
+// (consecutive ids on one XCD) put one global-row workgroup in every three among the first
+// 3*grid_rows ids when the main grid is at least twice as large, else the global-row workgroups
+// first.  The work of one workgroup is a generic lambda over its kind (MODE) and its index wg
+// among that kind's workgroups; the kernel arguments stay in the kernel argument segment.
+template <int D, int NW, int QB, int MODE_MAIN>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
+  __shared__ Smem<D> sm;
+  const FwdCore a = args;
+  const int total = gridDim.x;
+  const int Lid = xcd_remap(blockIdx.x, total);
+  const int n_rows_wg = a.grid_rows;
+  const int n_main_wg = total - n_rows_wg;
+  int gi = -1, mi = 0;
+  if (n_main_wg >= 2 * n_rows_wg) {
+    if (Lid % 3 == 2 && Lid / 3 < n_rows_wg) gi = Lid / 3;
+    else mi = Lid - min(n_rows_wg, (Lid + 1) / 3);
   } else {
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    b = L / a.tiles_per_b;
-    int r = L - b * a.tiles_per_b;
+    if (Lid < n_rows_wg) gi = Lid;
+    else mi = Lid - n_rows_wg;
+  }
+
+  // Main workgroups: batch sample, head, its dilation and the workgroup's index among the head's
+  // workgroups, from the per-head workgroup table (read here, in the kernel body, so that the
+  // table stays in the kernel argument segment).
+  int main_b = 0, main_h = 0, main_dl = 1, main_r = 0;
+  if (gi < 0) {
+    main_b = mi / a.tiles_per_b;
+    int r = mi - main_b * a.tiles_per_b;
     if (a.uniform_dil > 0) {
-      const int tph = a.tile_off[1];
-      h = r / tph;
-      r -= h * tph;
-      dl = a.uniform_dil;
+      const int tph = args.tile_off[1];
+      main_h = r / tph;
+      r -= main_h * tph;
+      main_dl = a.uniform_dil;
     } else {
       int lo = 0, hi = a.H - 1;  // last head with tile_off[h] <= r
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.tile_off[mid] <= r) lo = mid; else hi = mid - 1;
+        if (args.tile_off[mid] <= r) lo = mid; else hi = mid - 1;
       }
-      h = lo;
-      r -= a.tile_off[h];
-      dl = a.dil[h];
+      main_h = lo;
+      r -= args.tile_off[main_h];
+      main_dl = args.dil[main_h];
     }
-    if constexpr (MODE == kBand) {
-      for (;;) {  // residue class p holds ceil((n - p) / dl) positions
-        const int n_p = (a.n - p + dl - 1) / dl;
-        const int t_p = (n_p + QT - 1) / QT;
-        if (r < t_p) { np = n_p; break; }
-        r -= t_p;
-        ++p;
-      }
-      q0 = r * QT;
-    } else {
-      q0 = r * a.block;  // kLayout: query block r (QT == block)
-    }
+    main_r = r;
   }
-  // key stride of the local tiles (dilation of this head in window mode)
-  const int kst = (MODE == kBand) ? min(dl, a.n) : 1;
-  const long bh = (long)b * a.H + h;
-  const uint16_t* Qb = a.q + bh * a.n * D;
-  const uint16_t* Kb = a.k + bh * a.n * D;
-  const uint16_t* Vb = a.v + bh * a.n * D;
-  const uint8_t* pad = a.kpad ? a.kpad + (long)b * a.n : nullptr;
-  const int* gb = a.gidx ? a.gidx + (long)b * a.g : nullptr;
 
-  // ------------------------------------------------------------------ query rows of this lane
-  // Lane (qj, hh) holds query row wave*RW + 32qb + qj of the workgroup for every block qb.
-  int qpos[QB];  // sequence position, -1 = no such row
-  int qsub[QB];  // kBand: residue-subsequence index
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wave * RW + 32 * qb + qj;
-    qpos[qb] = -1;
-    qsub[qb] = 0;
-    if constexpr (MODE == kBand) {
-      qsub[qb] = q0 + qrow;
-      if (qsub[qb] < np) qpos[qb] = p + dl * qsub[qb];
-    } else if constexpr (MODE == kLayout) {
-      qpos[qb] = q0 + qrow;
+  auto body = [&](auto mode_c, const int wg) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int NT = NW * 64;
+    constexpr int RW = 32 * QB;        // query rows per wave
+    constexpr int QT = NW * RW;        // query rows per workgroup
+    constexpr int CH = D / 8;          // 16-byte chunks per row
+    constexpr int KS = D / 16;         // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;         // 32-row blocks of O^T
+    constexpr int MAT = kKeyTile * D * 2;
+    constexpr int NS = kStages<D>;
+    static_assert(NS == 2 || NS == 3, "stage count");
+    constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
+    constexpr int LPW = NLOAD / NW;    // of which each wave issues
+    constexpr int RPB = 64 / CH;       // rows per 1 KB block
+    constexpr int GREG = kGlobalCap / NT;
+    static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
+    static_assert(kGlobalCap % NT == 0, "global staging must split evenly");
+    constexpr bool kHasGlobalCols = MODE != kGlobalRows;
+
+    auto& stage_k = sm.stage_k;
+    auto& stage_v = sm.stage_v;
+    int* lay_list = sm.lay_list;
+    int& lay_cnt = sm.lay_cnt;
+    int* g_pos = sm.g_pos;
+    unsigned long long* g_valid = sm.g_valid;
+    unsigned long long* g_bits = sm.g_bits;
+    unsigned long long* pad_bits = sm.pad_bits;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int qj = lane & 31, hh = lane >> 5;
+
+    // ------------------------------------------------------------------ work decomposition
+    int b = 0, h = 0, dl = 1, p = 0, np = a.n, q0 = 0, ck = 0, rg = 0;
+    if constexpr (MODE == kGlobalRows) {
+      const int rgs = (a.g + QT - 1) / QT;
+      int x = wg;
+      ck = x % a.chunks;
+      x /= a.chunks;
+      rg = x % rgs;
+      x /= rgs;
+      h = x % a.H;
+      b = x / a.H;
     } else {
-      const int c = rg * QT + qrow;
-      if (c < a.g) {
-        const int x = gb[c];
-        if (x >= 0 && x < a.n) qpos[qb] = x;
+      (void)wg;
+      b = main_b;
+      h = main_h;
+      dl = main_dl;
+      int r = main_r;
+      if constexpr (MODE == kBand) {
+        for (;;) {  // residue class p holds ceil((n - p) / dl) positions
+          const int n_p = (a.n - p + dl - 1) / dl;
+          const int t_p = (n_p + QT - 1) / QT;
+          if (r < t_p) { np = n_p; break; }
+          r -= t_p;
+          ++p;
+        }
+        q0 = r * QT;
+      } else {
+        q0 = r * a.block;  // kLayout: query block r (QT == block)
       }
     }
-  }
-  // Q fragments (B operands of the score MFMAs), loaded once.
-  const float c2 = a.scale_log2;
-  u32x4 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qf[qb][s] = u32x4{0, 0, 0, 0};
-      if (qpos[qb] >= 0)
-        qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
-    }
-  // Consume the fragments here so that the compiler waits for these loads before the tile loop;
-  // otherwise it waits for them (vmcnt(0), which also drains the K/V prefetch) inside the loop.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
+    // key stride of the local tiles (dilation of this head in window mode)
+    const int kst = (MODE == kBand) ? min(dl, a.n) : 1;
+    const long bh = (long)b * a.H + h;
+    const uint16_t* Qb = a.q + bh * a.n * D;
+    const uint16_t* Kb = a.k + bh * a.n * D;
+    const uint16_t* Vb = a.v + bh * a.n * D;
+    const uint8_t* pad = a.kpad ? a.kpad + (long)b * a.n : nullptr;
+    const int* gb = a.gidx ? a.gidx + (long)b * a.g : nullptr;
 
-  // kGlobalRows also publishes, once per (batch, global column), the column's position and
-  // whether it is a usable key (in range, not padded) for the main kernel.
-  if constexpr (MODE == kGlobalRows) {
-    if (h == 0 && ck == 0 && hh == 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int c = rg * QT + wave * RW + 32 * qb + qj;
+    // ------------------------------------------------------------------ query rows of this lane
+    // Lane (qj, hh) holds query row wave*RW + 32qb + qj of the workgroup for every block qb.
+    int qpos[QB];  // sequence position, -1 = no such row
+    int qsub[QB];  // kBand: residue-subsequence index
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = wave * RW + 32 * qb + qj;
+      qpos[qb] = -1;
+      qsub[qb] = 0;
+      if constexpr (MODE == kBand) {
+        qsub[qb] = q0 + qrow;
+        if (qsub[qb] < np) qpos[qb] = p + dl * qsub[qb];
+      } else if constexpr (MODE == kLayout) {
+        qpos[qb] = q0 + qrow;
+      } else {
+        const int c = rg * QT + qrow;
         if (c < a.g) {
           const int x = gb[c];
-          const bool ok = x >= 0 && x < a.n && !(pad && pad[x]);
-          const int xc = min(max(x, 0), a.n);  // keeps the records ascending
-          a.gmeta[(long)b * a.g + c] = (int)((ok ? 0x80000000u : 0u) | (uint32_t)xc);
+          if (x >= 0 && x < a.n) qpos[qb] = x;
         }
       }
     }
-  }
-
-  // ------------------------------------------------------------------ key tiles
-  int n_local = 0, k_lo = 0, k_hi = -1, tpb = 1;
-  if constexpr (MODE == kBand) {
-    if (a.band_on) {
-      const int q_last = min(q0 + QT, np) - 1;
-      k_lo = max(0, q0 - a.wl);
-      k_hi = min(np - 1, q_last + a.wr);
-      n_local = (k_hi >= k_lo) ? (k_hi - k_lo + kKeyTile) / kKeyTile : 0;
-    }
-  } else if constexpr (MODE == kLayout) {
-    tpb = a.block / kKeyTile;
-    if (wave == 0) {  // compact the valid block ids of this row into LDS
-      const int nb = a.n / a.block;
-      const int* row = a.layout + ((long)h * nb + q0 / a.block) * a.max_kb;
-      int base = 0;
-      for (int e0 = 0; e0 < a.max_kb; e0 += 64) {
-        const int e = e0 + lane;
-        int id = (e < a.max_kb) ? row[e] : -1;
-        if (id >= nb) id = -1;  // out-of-range ids are ignored rather than read
-        const unsigned long long m = __ballot(id >= 0);
-        if (id >= 0) lay_list[base + __popcll(m & ((1ull << lane) - 1ull))] = id;
-        base += __popcll(m);
+    // Q fragments (B operands of the score MFMAs), loaded once.
+    const float c2 = a.scale_log2;
+    u32x4 qf[QB][KS];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        qf[qb][s] = u32x4{0, 0, 0, 0};
+        if (qpos[qb] >= 0)
+          qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
       }
-      if (lane == 0) lay_cnt = base;
+    // Consume the fragments here so that the compiler waits for these loads before the tile loop;
+    // otherwise it waits for them (vmcnt(0), which also drains the K/V prefetch) inside the loop.
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
+
+    // ------------------------------------------------------------------ key tiles
+    int n_local = 0, k_lo = 0, k_hi = -1, tpb = 1;
+    if constexpr (MODE == kBand) {
+      if (a.band_on) {
+        const int q_last = min(q0 + QT, np) - 1;
+        k_lo = max(0, q0 - a.wl);
+        k_hi = min(np - 1, q_last + a.wr);
+        n_local = (k_hi >= k_lo) ? (k_hi - k_lo + kKeyTile) / kKeyTile : 0;
+      }
+    } else if constexpr (MODE == kLayout) {
+      tpb = a.block / kKeyTile;
+      if (wave == 0) {  // compact the valid block ids of this row into LDS
+        const int nb = a.n / a.block;
+        const int* row = a.layout + ((long)h * nb + q0 / a.block) * a.max_kb;
+        int base = 0;
+        for (int e0 = 0; e0 < a.max_kb; e0 += 64) {
+          const int e = e0 + lane;
+          int id = (e < a.max_kb) ? row[e] : -1;
+          if (id >= nb) id = -1;  // out-of-range ids are ignored rather than read
+          const unsigned long long m = __ballot(id >= 0);
+          if (id >= 0) lay_list[base + __popcll(m & ((1ull << lane) - 1ull))] = id;
+          base += __popcll(m);
+        }
+        if (lane == 0) lay_cnt = base;
+      }
+      __syncthreads();
+      n_local = lay_cnt * tpb;
+    } else {
+      const int c0 = ck * kGlobalChunk;
+      const int c1 = min(a.n, c0 + kGlobalChunk);
+      n_local = (c1 > c0) ? (c1 - c0 + kKeyTile - 1) / kKeyTile : 0;
+      k_lo = c0;
+      k_hi = c1 - 1;
+    }
+    const int n_gtiles = (kHasGlobalCols && a.g > 0) ? (a.g + kKeyTile - 1) / kKeyTile : 0;
+    const int n_tiles = n_local + n_gtiles;
+
+    auto tile_of = [&](int t) -> Tile {
+      Tile T;
+      T.ks0 = 0;
+      if (t >= n_local) {
+        T.gathered = 1;
+        T.base = (t - n_local) * kKeyTile;
+        T.count = min(kKeyTile, a.g - T.base);
+      } else if constexpr (MODE == kBand) {
+        T.gathered = 0;
+        T.ks0 = k_lo + t * kKeyTile;
+        T.base = p + dl * T.ks0;
+        T.count = min(kKeyTile, np - T.ks0);
+      } else if constexpr (MODE == kLayout) {
+        T.gathered = 0;
+        T.base = lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
+        T.count = kKeyTile;
+      } else {
+        T.gathered = 0;
+        T.base = k_lo + t * kKeyTile;
+        T.count = min(kKeyTile, k_hi + 1 - T.base);
+      }
+      return T;
+    };
+
+    // ------------------------------------------------------------------ staging in LDS
+    // Global-key columns: position and validity, once per workgroup.  A usable global key is
+    // attended through the global-column tiles by every query, so in window mode the local tiles
+    // drop it (each edge is counted once): g_bits marks the global keys among the window keys,
+    // bit i of word t for residue index k_lo + 64t + i, when the window range fits; otherwise
+    // each local tile searches the sorted positions.
+    const bool gbits_staged = MODE == kBand && n_gtiles > 0 && n_local <= kPadWords;
+    if constexpr (kHasGlobalCols) {
+      if (n_gtiles > 0) {
+        if constexpr (MODE == kBand) {
+          if (gbits_staged) {
+            for (int w = tid; w < n_local; w += NT) g_bits[w] = 0ull;
+            __syncthreads();
+          }
+        }
+  #pragma unroll
+        for (int i = 0; i < GREG; ++i) {
+          const int c = tid + NT * i;
+          const int x = (c < a.g) ? gb[c] : a.n;
+          bool ok = x >= 0 && x < a.n;         // a usable key: in range and not padded
+          if (ok && pad) ok = pad[x] == 0;
+          const int pos = min(max(x, 0), a.n);  // keeps the positions ascending
+          if constexpr (MODE == kLayout) {
+            // a global key inside one of this row's layout blocks is attended through the block
+            const int blk = pos / a.block;
+            for (int e = 0; e < lay_cnt; ++e) ok = ok && (lay_list[e] != blk);
+          }
+          if constexpr (MODE == kBand) {
+            const int rel = pos - p;
+            if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
+              const int j = rel / dl - k_lo;
+              if (j >= 0 && j < kKeyTile * n_local) atomicOr(&g_bits[j >> 6], 1ull << (j & 63));
+            }
+          }
+          g_pos[c] = pos;
+          const unsigned long long vm = __ballot(ok);
+          if (lane == 0) g_valid[c >> 6] = vm;
+        }
+      }
+    }
+    // Key padding of the positions the local tiles can reach, as bits (bit i of word w: position
+    // pad_lo + 64w + i is a usable key), when they fit; otherwise each tile reads its pad bytes.
+    int pad_lo = 0;
+    bool pad_staged = false;
+    if (pad && n_local > 0) {
+      long lo, hi;
+      if constexpr (MODE == kBand) {
+        lo = p + (long)dl * k_lo;
+        hi = min((long)a.n - 1, p + (long)dl * (k_lo + (long)kKeyTile * n_local - 1));
+      } else if constexpr (MODE == kLayout) {
+        lo = 0;
+        hi = a.n - 1;
+      } else {
+        lo = k_lo;
+        hi = k_hi;
+      }
+      lo &= ~63L;
+      const long words = ((hi - lo) >> 6) + 1;
+      pad_staged = words <= kPadWords;
+      pad_lo = (int)lo;
+      if (pad_staged) {
+        for (int w = wave; w < (int)words; w += NW) {
+          const int pos = pad_lo + 64 * w + lane;
+          const bool ok = pos < a.n && pad[pos] == 0;
+          const unsigned long long m = __ballot(ok);
+          if (lane == 0) pad_bits[w] = m;
+        }
+      }
     }
     __syncthreads();
-    n_local = lay_cnt * tpb;
-  } else {
-    const int c0 = ck * kGlobalChunk;
-    const int c1 = min(a.n, c0 + kGlobalChunk);
-    n_local = (c1 > c0) ? (c1 - c0 + kKeyTile - 1) / kKeyTile : 0;
-    k_lo = c0;
-    k_hi = c1 - 1;
-  }
-  const int n_gtiles = (kHasGlobalCols && a.g > 0) ? (a.g + kKeyTile - 1) / kKeyTile : 0;
-  const int n_tiles = n_local + n_gtiles;
 
-  auto tile_of = [&](int t) -> Tile {
-    Tile T;
-    T.ks0 = 0;
-    if (t >= n_local) {
-      T.gathered = 1;
-      T.base = (t - n_local) * kKeyTile;
-      T.count = min(kKeyTile, a.g - T.base);
-    } else if constexpr (MODE == kBand) {
-      T.gathered = 0;
-      T.ks0 = k_lo + t * kKeyTile;
-      T.base = p + dl * T.ks0;
-      T.count = min(kKeyTile, np - T.ks0);
-    } else if constexpr (MODE == kLayout) {
-      T.gathered = 0;
-      T.base = lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
-      T.count = kKeyTile;
-    } else {
-      T.gathered = 0;
-      T.base = k_lo + t * kKeyTile;
-      T.count = min(kKeyTile, k_hi + 1 - T.base);
-    }
-    return T;
-  };
-
-  // ------------------------------------------------------------------ staging in LDS
-  // Global-key columns: position and validity, once per workgroup.  A usable global key is
-  // attended through the global-column tiles by every query, so in window mode the local tiles
-  // drop it (each edge is counted once): g_bits marks the global keys among the window keys,
-  // bit i of word t for residue index k_lo + 64t + i, when the window range fits; otherwise
-  // each local tile searches the sorted positions.
-  const bool gbits_staged = MODE == kBand && n_gtiles > 0 && n_local <= kPadWords;
-  if constexpr (kHasGlobalCols) {
-    if (n_gtiles > 0) {
-      if constexpr (MODE == kBand) {
-        if (gbits_staged) {
-          for (int w = tid; w < n_local; w += NT) g_bits[w] = 0ull;
-          __syncthreads();
+    // ------------------------------------------------------------------ tile loading
+    // Wave w moves the 1 KB blocks w*LPW .. w*LPW + LPW - 1 of a tile: all of one matrix (K for
+    // the first half of the waves, the "K waves", V for the rest).  Block `sub` of a matrix holds
+    // rows RPB*sub .. RPB*sub + RPB - 1; lane l moves row RPB*sub + l/CH, 16-byte chunk l%CH, to
+    // LDS byte sub*1024 + 16*l (the chunk's swizzled slot in that row).
+    const int mat = (wave * LPW) / CH;
+    const int sub0 = (wave * LPW) % CH;
+    auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
+    auto ld_col = [&](int j) -> int {
+      const int row = ld_row(j);
+      return 8 * ((lane % CH) ^ (mat == 0 ? swz_k<D>(row) : swz_v<D>(row)));
+    };
+    // byte offsets of this lane's chunks within a local tile starting at row 0 (rows past the
+    // sequence end land at or beyond the resource size, so they read zeros)
+    uint32_t voff[LPW];
+  #pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
+    const uint16_t* msrc = (mat == 0) ? Kb : Vb;
+    auto issue = [&](unsigned char* st, const Tile& T) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + sub0 * 1024));
+      if (kHasGlobalCols && T.gathered) {
+        const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
+  #pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const int pos = g_pos[T.base + min(ld_row(j), T.count - 1)];
+          lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
         }
+      } else {
+        const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
+  #pragma unroll
+        for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
       }
-#pragma unroll
-      for (int i = 0; i < GREG; ++i) {
-        const int c = tid + NT * i;
-        const int m = (c < a.g) ? a.gmeta[(long)b * a.g + c] : a.n;
-        bool ok = c < a.g && m < 0;  // bit 31: usable key
-        const int pos = m & 0x7fffffff;
-        if constexpr (MODE == kLayout) {
-          // a global key inside one of this row's layout blocks is attended through the block
-          const int blk = pos / a.block;
-          for (int e = 0; e < lay_cnt; ++e) ok = ok && (lay_list[e] != blk);
-        }
-        if constexpr (MODE == kBand) {
-          const int rel = pos - p;
-          if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
-            const int j = rel / dl - k_lo;
-            if (j >= 0 && j < kKeyTile * n_local) atomicOr(&g_bits[j >> 6], 1ull << (j & 63));
-          }
-        }
-        g_pos[c] = pos;
-        const unsigned long long vm = __ballot(ok);
-        if (lane == 0) g_valid[c >> 6] = vm;
+    };
+    // window mode: bits of the usable global keys among the rows of local tile t
+    auto global_keys = [&](const Tile& T, int t) -> unsigned long long {
+      if (n_gtiles == 0) return 0ull;
+      if (gbits_staged) return g_bits[t];
+      const bool in = lane < T.count;
+      const int pos = in ? T.base + kst * lane : 0;
+      int c = -1;  // last column with position <= pos (positions ascend)
+  #pragma unroll
+      for (int step = kGlobalCap; step > 0; step >>= 1)
+        if (c + step < a.g && g_pos[c + step] <= pos) c += step;
+      const bool hit = in && c >= 0 && g_pos[c] == pos && ((g_valid[c >> 6] >> (c & 63)) & 1ull);
+      return __ballot(hit);
+    };
+    // allowed-key bits of a local tile (bit r: row r exists and is not padded)
+    auto local_valid = [&](const Tile& T) -> unsigned long long {
+      if (!pad) return T.count >= 64 ? ~0ull : ((1ull << T.count) - 1ull);
+      const bool in = lane < T.count;
+      const long pos = in ? (long)T.base + (long)kst * lane : 0;
+      bool ok;
+      if (pad_staged) {
+        const int rel = in ? (int)(pos - pad_lo) : 0;
+        ok = in && ((pad_bits[rel >> 6] >> (rel & 63)) & 1ull);
+      } else {
+        ok = in && pad[pos] == 0;
       }
-    }
-  }
-  // Key padding of the positions the local tiles can reach, as bits (bit i of word w: position
-  // pad_lo + 64w + i is a usable key), when they fit; otherwise each tile reads its pad bytes.
-  int pad_lo = 0;
-  bool pad_staged = false;
-  if (pad && n_local > 0) {
-    long lo, hi;
-    if constexpr (MODE == kBand) {
-      lo = p + (long)dl * k_lo;
-      hi = min((long)a.n - 1, p + (long)dl * (k_lo + (long)kKeyTile * n_local - 1));
-    } else if constexpr (MODE == kLayout) {
-      lo = 0;
-      hi = a.n - 1;
-    } else {
-      lo = k_lo;
-      hi = k_hi;
-    }
-    lo &= ~63L;
-    const long words = ((hi - lo) >> 6) + 1;
-    pad_staged = words <= kPadWords;
-    pad_lo = (int)lo;
-    if (pad_staged) {
-      for (int w = wave; w < (int)words; w += NW) {
-        const int pos = pad_lo + 64 * w + lane;
-        const bool ok = pos < a.n && pad[pos] == 0;
-        const unsigned long long m = __ballot(ok);
-        if (lane == 0) pad_bits[w] = m;
-      }
-    }
-  }
-  __syncthreads();
+      return __ballot(ok);
+    };
 
-  // ------------------------------------------------------------------ tile loading
-  // Wave w moves the 1 KB blocks w*LPW .. w*LPW + LPW - 1 of a tile: all of one matrix (K for
-  // the first half of the waves, the "K waves", V for the rest).  Block `sub` of a matrix holds
-  // rows RPB*sub .. RPB*sub + RPB - 1; lane l moves row RPB*sub + l/CH, 16-byte chunk l%CH, to
-  // LDS byte sub*1024 + 16*l (the chunk's swizzled slot in that row).
-  const int mat = (wave * LPW) / CH;
-  const int sub0 = (wave * LPW) % CH;
-  auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
-  auto ld_col = [&](int j) -> int {
-    const int row = ld_row(j);
-    return 8 * ((lane % CH) ^ (mat == 0 ? swz_k<D>(row) : swz_v<D>(row)));
-  };
-  // byte offsets of this lane's chunks within a local tile starting at row 0 (rows past the
-  // sequence end land at or beyond the resource size, so they read zeros)
-  uint32_t voff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j)
-    voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
-  const uint16_t* msrc = (mat == 0) ? Kb : Vb;
-  auto issue = [&](unsigned char* st, const Tile& T) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + sub0 * 1024));
-    if (kHasGlobalCols && T.gathered) {
-      const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int pos = g_pos[T.base + min(ld_row(j), T.count - 1)];
-        lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
-      }
-    } else {
-      const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
-    }
-  };
-  // window mode: bits of the usable global keys among the rows of local tile t
-  auto global_keys = [&](const Tile& T, int t) -> unsigned long long {
-    if (n_gtiles == 0) return 0ull;
-    if (gbits_staged) return g_bits[t];
-    const bool in = lane < T.count;
-    const int pos = in ? T.base + kst * lane : 0;
-    int c = -1;  // last column with position <= pos (positions ascend)
-#pragma unroll
-    for (int step = kGlobalCap; step > 0; step >>= 1)
-      if (c + step < a.g && g_pos[c + step] <= pos) c += step;
-    const bool hit = in && c >= 0 && g_pos[c] == pos && ((g_valid[c >> 6] >> (c & 63)) & 1ull);
-    return __ballot(hit);
-  };
-  // allowed-key bits of a local tile (bit r: row r exists and is not padded)
-  auto local_valid = [&](const Tile& T) -> unsigned long long {
-    if (!pad) return T.count >= 64 ? ~0ull : ((1ull << T.count) - 1ull);
-    const bool in = lane < T.count;
-    const long pos = in ? (long)T.base + (long)kst * lane : 0;
-    bool ok;
-    if (pad_staged) {
-      const int rel = in ? (int)(pos - pad_lo) : 0;
-      ok = in && ((pad_bits[rel >> 6] >> (rel & 63)) & 1ull);
-    } else {
-      ok = in && pad[pos] == 0;
-    }
-    return __ballot(ok);
-  };
-
-  // ------------------------------------------------------------------ per-lane LDS read offsets
-  // K operand of S^T for key block kb, k-step ks: row 32kb + qj, logical chunk 2ks + hh.
-  // V^T operand for 16-key group t, d block db, half r: transposing read; lane l of 16-lane group
-  // G = l/16 supplies row 16t + 8r + 4(l/32) + (l%16)/4 at d = 32db + 16(G%2) + 4(l%4) and gets
-  // V[16t + 8r + 4(l/32) + e][32db + l%32], e = 0..3.
-  const int ksw = swz_k<D>(qj);  // the same for rows qj and 32 + qj
-  int koff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = qj * (2 * D) + (((2 * ks + hh) ^ ksw) * 16);
-  const int vi = lane & 15, vg = lane >> 4;
-  const int vrow0 = 4 * hh + (vi >> 2);
-  const int vsw = swz_v<D>(vrow0);
-  int voffs[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int chunk = 4 * db + 2 * (vg & 1) + ((vi & 3) >> 1);
-    voffs[db] = vrow0 * (2 * D) + ((chunk ^ vsw) * 16) + 8 * (vi & 1);
-  }
-
-  // ------------------------------------------------------------------ running state
-  // Per row: ref = the exponent offset all weights of the row are taken against (log2 units),
-  // has = some allowed key has been seen, l = sum of the weights 2^(c2 s - ref), o = the weighted
-  // sum of value rows (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4).
-  f32x16 o[QB][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-  float ref[QB], l_run[QB];
-  bool has[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    ref[qb] = 0.f;
-    l_run[qb] = 0.f;
-    has[qb] = false;
-  }
-
-  // wave row range (kBand tile skipping)
-  const int w_first = q0 + wave * RW;
-  const int w_last = (MODE == kBand) ? min(w_first + RW - 1, np - 1) : w_first + RW - 1;
-  bool wave_rows;
-  if constexpr (MODE == kBand) wave_rows = w_first < np;
-  else if constexpr (MODE == kLayout) wave_rows = true;
-  else wave_rows = (rg * QT + wave * RW) < a.g;
-
-  // ------------------------------------------------------------------ one tile
-  // ---- raw scores S^T = K Q^T of both 32-key halves of a K tile, for every query block
-  auto scores = [&](const unsigned char* st, f32x16 (&sc)[2][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(st + koff[ks] + kb * 32 * (2 * D));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma_32x32x16(kf, qf[qb][ks], sc[kb][qb]);
-      }
-    }
-  };
-  // ---- masks, online softmax step and O^T += V^T P^T for one tile whose scores are in sc.
-  // Per-element masks (key validity bits and, in window mode, the band edges) are applied only
-  // when some key of the tile is excluded for some row of the wave; interior tiles skip them.
-  auto finish = [&](f32x16 (&sc)[2][QB], const unsigned char* st, const Tile& T,
-                    unsigned long long vmask, bool need_band) {
-    // ---- masks.  Register r of half kb holds key 32kb + 8(r/4) + 4hh + r%4, i.e. bit
-    // 8(r/4) + r%4 of w = (the tile's allowed keys for this lane's query) >> (32kb + 4hh).
-    if (need_band || vmask != ~0ull) {
-      const float ninf = neg_inf();
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        unsigned long long m = vmask >> (4 * hh);
-        if (need_band) {
-          // keys k with qs - wl <= ks0 + k <= qs + wr, shifted by this lane's 4*hh
-          const int lo = qsub[qb] - a.wl - T.ks0 - 4 * hh;
-          const int hi = qsub[qb] + a.wr - T.ks0 - 4 * hh;
-          unsigned long long bm = 0ull;
-          if (hi >= 0 && lo <= 63) {
-            const int lc = max(lo, 0), hc = min(hi, 63);
-            bm = (~0ull >> (63 - (hc - lc))) << lc;
-          }
-          m &= bm;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint32_t w = (uint32_t)(m >> (32 * kb));
-          asm("" : "+v"(w));  // per-lane word: the selects below stay two VALU ops each
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sc[kb][qb][r] = keep_if_bit(sc[kb][qb][r], w, 8 * (r >> 2) + (r & 3), ninf);
-        }
-      }
+    // ------------------------------------------------------------------ per-lane LDS read offsets
+    // K operand of S^T for key block kb, k-step ks: row 32kb + qj, logical chunk 2ks + hh.
+    // V^T operand for 16-key group t, d block db, half r: transposing read; lane l of 16-lane group
+    // G = l/16 supplies row 16t + 8r + 4(l/32) + (l%16)/4 at d = 32db + 16(G%2) + 4(l%4) and gets
+    // V[16t + 8r + 4(l/32) + e][32db + l%32], e = 0..3.
+    const int ksw = swz_k<D>(qj);  // the same for rows qj and 32 + qj
+    int koff[KS];
+  #pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = qj * (2 * D) + (((2 * ks + hh) ^ ksw) * 16);
+    const int vi = lane & 15, vg = lane >> 4;
+    const int vrow0 = 4 * hh + (vi >> 2);
+    const int vsw = swz_v<D>(vrow0);
+    int voffs[DB];
+  #pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * (vg & 1) + ((vi & 3) >> 1);
+      voffs[db] = vrow0 * (2 * D) + ((chunk ^ vsw) * 16) + 8 * (vi & 1);
     }
 
-    // ---- online softmax step over the 64 keys.  Weights are 2^(c2 s - ref), c2 = scale *
-    // log2(e).  ref only moves when a row sees its first allowed key (then ref := that tile's row
-    // max) or when a row's max exceeds ref by more than 2^8; otherwise every weight stays below
-    // 2^8, which fp32 and bf16 hold without loss, and the final normalisation by l makes the
-    // result exact.  In the common case no row moves: each weight is one FMA and one exp2.
-    float xm[QB];
-    bool need[QB];
-    bool need_any = false;
-#pragma unroll
+    // ------------------------------------------------------------------ running state
+    // Per row: ref = the exponent offset all weights of the row are taken against (log2 units),
+    // has = some allowed key has been seen, l = sum of the weights 2^(c2 s - ref), o = the weighted
+    // sum of value rows (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4).
+    f32x16 o[QB][DB];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+    float ref[QB], l_run[QB];
+    bool has[QB];
+  #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const f32x16& u = sc[0][qb];
-      const f32x16& v = sc[1][qb];
-      float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
-      float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), u[15]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[0]), v[1]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[2]), v[3]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[4]), v[5]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[6]), v[7]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[8]), v[9]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[10]), v[11]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[12]), v[13]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[14]), __builtin_fmaxf(x1, v[15]));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
-                                                       false, false);
-      const float x = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
-      xm[qb] = x;
-      need[qb] = (x != neg_inf()) & (!has[qb] | (x - ref[qb] > kRescaleLog2));
-      need_any = need_any | need[qb];
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
-      // some row moves its reference (rare): per lane, the new reference is the row max if the
-      // row moves, else the old one
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nref = need[qb] ? xm[qb] : ref[qb];
-        const float alpha = has[qb] ? exp2_fast(ref[qb] - nref) : 1.f;  // old weights rescaled
-        ref[qb] = nref;
-        has[qb] = has[qb] || need[qb];
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-      }
+      ref[qb] = 0.f;
+      l_run[qb] = 0.f;
+      has[qb] = false;
     }
 
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint32_t pk[QB][8];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nr = -ref[qb];
-        float la = 0.f, lb = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
-          const float p1 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 1], c2, nr));
-          const float p2 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 2], c2, nr));
-          const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
-          pk[qb][r >> 1] = pack_bf16x2(p0, p1);
-          pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
-          la += p0 + p1;
-          lb += p2 + p3;
+    // wave row range (kBand tile skipping)
+    const int w_first = q0 + wave * RW;
+    const int w_last = (MODE == kBand) ? min(w_first + RW - 1, np - 1) : w_first + RW - 1;
+    bool wave_rows;
+    if constexpr (MODE == kBand) wave_rows = w_first < np;
+    else if constexpr (MODE == kLayout) wave_rows = true;
+    else wave_rows = (rg * QT + wave * RW) < a.g;
+
+    // ------------------------------------------------------------------ one tile
+    // ---- raw scores S^T = K Q^T of both 32-key halves of a K tile, for every query block
+    auto scores = [&](const unsigned char* st, f32x16 (&sc)[2][QB]) {
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(st + koff[ks] + kb * 32 * (2 * D));
+  #pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma_32x32x16(kf, qf[qb][ks], sc[kb][qb]);
         }
-        l_run[qb] += la + lb;
       }
-      // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
-#pragma unroll
-      for (int gh = 0; gh < 2; ++gh) {
-        const int g = 2 * kb + gh;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const unsigned char* vp = st + voffs[db] + 16 * g * (2 * D);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp));
-          const s16x4 v1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp + 8 * (2 * D)));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-          const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4 bp = {pk[qb][4 * gh + 0], pk[qb][4 * gh + 1], pk[qb][4 * gh + 2],
-                              pk[qb][4 * gh + 3]};
-            o[qb][db] = mfma_32x32x16(va, bp, o[qb][db]);
+    };
+    // ---- masks, online softmax step and O^T += V^T P^T for one tile whose scores are in sc.
+    // Per-element masks (key validity bits and, in window mode, the band edges) are applied only
+    // when some key of the tile is excluded for some row of the wave; interior tiles skip them.
+    auto finish = [&](f32x16 (&sc)[2][QB], const unsigned char* st, const Tile& T,
+                      unsigned long long vmask, bool need_band) {
+      // ---- masks.  Register r of half kb holds key 32kb + 8(r/4) + 4hh + r%4, i.e. bit
+      // 8(r/4) + r%4 of w = (the tile's allowed keys for this lane's query) >> (32kb + 4hh).
+      if (need_band || vmask != ~0ull) {
+        const float ninf = neg_inf();
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          unsigned long long m = vmask >> (4 * hh);
+          if (need_band) {
+            // keys k with qs - wl <= ks0 + k <= qs + wr, shifted by this lane's 4*hh
+            const int lo = qsub[qb] - a.wl - T.ks0 - 4 * hh;
+            const int hi = qsub[qb] + a.wr - T.ks0 - 4 * hh;
+            unsigned long long bm = 0ull;
+            if (hi >= 0 && lo <= 63) {
+              const int lc = max(lo, 0), hc = min(hi, 63);
+              bm = (~0ull >> (63 - (hc - lc))) << lc;
+            }
+            m &= bm;
+          }
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            uint32_t w = (uint32_t)(m >> (32 * kb));
+            asm("" : "+v"(w));  // per-lane word: the selects below stay two VALU ops each
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sc[kb][qb][r] = keep_if_bit(sc[kb][qb][r], w, 8 * (r >> 2) + (r & 3), ninf);
           }
         }
       }
+
+      // ---- online softmax step over the 64 keys.  Weights are 2^(c2 s - ref), c2 = scale *
+      // log2(e).  ref only moves when a row sees its first allowed key (then ref := that tile's row
+      // max) or when a row's max exceeds ref by more than 2^8; otherwise every weight stays below
+      // 2^8, which fp32 and bf16 hold without loss, and the final normalisation by l makes the
+      // result exact.  In the common case no row moves: each weight is one FMA and one exp2.
+      float xm[QB];
+      bool need[QB];
+      bool need_any = false;
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const f32x16& u = sc[0][qb];
+        const f32x16& v = sc[1][qb];
+        float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
+        float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), u[15]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[0]), v[1]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[2]), v[3]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[4]), v[5]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[6]), v[7]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[8]), v[9]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[10]), v[11]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[12]), v[13]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[14]), __builtin_fmaxf(x1, v[15]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
+                                                         false, false);
+        const float x = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+        xm[qb] = x;
+        need[qb] = (x != neg_inf()) & (!has[qb] | (x - ref[qb] > kRescaleLog2));
+        need_any = need_any | need[qb];
+      }
+      if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
+        // some row moves its reference (rare): per lane, the new reference is the row max if the
+        // row moves, else the old one
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float nref = need[qb] ? xm[qb] : ref[qb];
+          const float alpha = has[qb] ? exp2_fast(ref[qb] - nref) : 1.f;  // old weights rescaled
+          ref[qb] = nref;
+          has[qb] = has[qb] || need[qb];
+          l_run[qb] *= alpha;
+  #pragma unroll
+          for (int db = 0; db < DB; ++db)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+        }
+      }
+
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t pk[QB][8];
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float nr = -ref[qb];
+          float la = 0.f, lb = 0.f;
+  #pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
+            const float p1 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 1], c2, nr));
+            const float p2 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 2], c2, nr));
+            const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
+            pk[qb][r >> 1] = pack_bf16x2(p0, p1);
+            pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
+            la += p0 + p1;
+            lb += p2 + p3;
+          }
+          l_run[qb] += la + lb;
+        }
+        // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
+  #pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {
+          const int g = 2 * kb + gh;
+  #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const unsigned char* vp = st + voffs[db] + 16 * g * (2 * D);
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp));
+            const s16x4 v1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp + 8 * (2 * D)));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+  #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              const u32x4 bp = {pk[qb][4 * gh + 0], pk[qb][4 * gh + 1], pk[qb][4 * gh + 2],
+                                pk[qb][4 * gh + 3]};
+              o[qb][db] = mfma_32x32x16(va, bp, o[qb][db]);
+            }
+          }
+        }
+      }
+    };
+    // Does tile T hold keys in reach of this wave's rows (window mode), and do band edges cut it?
+    auto reach = [&](const Tile& T, bool& need_band) -> bool {
+      need_band = false;
+      if (!wave_rows) return false;
+      if constexpr (MODE == kBand) {
+        if (!T.gathered) {
+          const int kf = T.ks0, kl = T.ks0 + kKeyTile - 1;
+          if (kl < w_first - a.wl || kf > w_last + a.wr) return false;
+          need_band = !(kf >= w_last - a.wl && kl <= w_first + a.wr);
+        }
+      }
+      return true;
+    };
+
+    // ------------------------------------------------------------------ tile loop
+    // NS LDS stages of K tiles and NS of V tiles; tile t lives in stage t % NS while tiles
+    // t+1 .. t+NS-1 stream into the others.  At the top of step t each wave waits for its own
+    // loads of tile t (later tiles' loads stay in flight: loads complete in issue order), then the
+    // barrier makes tile t visible to every wave and retires every read of stage (t-1) % NS, which
+    // is refilled with tile t+NS-1 right after.
+    const bool kwave = mat == 0;
+    if (n_tiles > 0) {
+  #pragma unroll
+      for (int i = 0; i < NS - 1; ++i)
+        if (i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
+      int st = 0;  // stage of tile t
+      for (int t = 0; t < n_tiles; ++t) {
+        if (NS == 3 && t + 1 < n_tiles) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const int stp = (st == 0) ? NS - 1 : st - 1;  // stage of tile t-1 (= that of t+NS-1)
+        if (t + NS - 1 < n_tiles) issue(kwave ? stage_k[stp] : stage_v[stp], tile_of(t + NS - 1));
+        const Tile T = tile_of(t);
+        bool need_band = false;
+        if (reach(T, need_band)) {
+          unsigned long long vmask;
+          if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, t);
+          else if constexpr (kHasGlobalCols) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T);
+          else vmask = local_valid(T);
+          f32x16 sc[2][QB];
+          scores(stage_k[st], sc);
+          finish(sc, stage_v[st], T, vmask, need_band);
+        }
+        st = (st + 1 == NS) ? 0 : st + 1;
+      }
+    }
+
+    // ------------------------------------------------------------------ epilogue
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = l_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(l_run[qb]), 32));
+      if (qpos[qb] < 0) continue;
+      if constexpr (MODE == kGlobalRows) {
+        const int c = rg * QT + wave * RW + 32 * qb + qj;
+        const long slot = (bh * a.g + c) * a.chunks + ck;
+        float* po = a.part + slot * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d = 32 * db + 8 * rq + 4 * hh;
+            *reinterpret_cast<float4*>(po + d) =
+                make_float4(o[qb][db][4 * rq], o[qb][db][4 * rq + 1], o[qb][db][4 * rq + 2],
+                            o[qb][db][4 * rq + 3]);
+          }
+        if (hh == 0) {
+          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
+          pml[0] = has[qb] ? ref[qb] : neg_inf();
+          pml[1] = l_tot;
+        }
+      } else {
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        uint16_t* orow = a.out + (bh * a.n + qpos[qb]) * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d = 32 * db + 8 * rq + 4 * hh;
+            u32x2 w;
+            w[0] = pack_bf16x2(o[qb][db][4 * rq] * inv, o[qb][db][4 * rq + 1] * inv);
+            w[1] = pack_bf16x2(o[qb][db][4 * rq + 2] * inv, o[qb][db][4 * rq + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + d) = w;
+          }
+        if (a.lse && hh == 0)
+          a.lse[bh * a.n + qpos[qb]] =
+              (l_tot > 0.f) ? (ref[qb] + __log2f(l_tot)) * kLn2 : neg_inf();
+      }
     }
   };
-  // Does tile T hold keys in reach of this wave's rows (window mode), and do band edges cut it?
-  auto reach = [&](const Tile& T, bool& need_band) -> bool {
-    need_band = false;
-    if (!wave_rows) return false;
-    if constexpr (MODE == kBand) {
-      if (!T.gathered) {
-        const int kf = T.ks0, kl = T.ks0 + kKeyTile - 1;
-        if (kl < w_first - a.wl || kf > w_last + a.wr) return false;
-        need_band = !(kf >= w_last - a.wl && kl <= w_first + a.wr);
-      }
-    }
-    return true;
-  };
-
-  // ------------------------------------------------------------------ tile loop
-  // NS LDS stages of K tiles and NS of V tiles; tile t lives in stage t % NS while tiles
-  // t+1 .. t+NS-1 stream into the others.  At the top of step t each wave waits for its own
-  // loads of tile t (later tiles' loads stay in flight: loads complete in issue order), then the
-  // barrier makes tile t visible to every wave and retires every read of stage (t-1) % NS, which
-  // is refilled with tile t+NS-1 right after.
-  const bool kwave = mat == 0;
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
-    int st = 0;  // stage of tile t
-    for (int t = 0; t < n_tiles; ++t) {
-      if (NS == 3 && t + 1 < n_tiles) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      const int stp = (st == 0) ? NS - 1 : st - 1;  // stage of tile t-1 (= that of t+NS-1)
-      if (t + NS - 1 < n_tiles) issue(kwave ? stage_k[stp] : stage_v[stp], tile_of(t + NS - 1));
-      const Tile T = tile_of(t);
-      bool need_band = false;
-      if (reach(T, need_band)) {
-        unsigned long long vmask;
-        if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, t);
-        else if constexpr (kHasGlobalCols) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T);
-        else vmask = local_valid(T);
-        f32x16 sc[2][QB];
-        scores(stage_k[st], sc);
-        finish(sc, stage_v[st], T, vmask, need_band);
-      }
-      st = (st + 1 == NS) ? 0 : st + 1;
-    }
-  }
-
-  // ------------------------------------------------------------------ epilogue
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(l_run[qb]), 32));
-    if (qpos[qb] < 0) continue;
-    if constexpr (MODE == kGlobalRows) {
-      const int c = rg * QT + wave * RW + 32 * qb + qj;
-      const long slot = (bh * a.g + c) * a.chunks + ck;
-      float* po = a.part + slot * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d = 32 * db + 8 * rq + 4 * hh;
-          *reinterpret_cast<float4*>(po + d) =
-              make_float4(o[qb][db][4 * rq], o[qb][db][4 * rq + 1], o[qb][db][4 * rq + 2],
-                          o[qb][db][4 * rq + 3]);
-        }
-      if (hh == 0) {
-        float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
-        pml[0] = has[qb] ? ref[qb] : neg_inf();
-        pml[1] = l_tot;
-      }
-    } else {
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      uint16_t* orow = a.out + (bh * a.n + qpos[qb]) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d = 32 * db + 8 * rq + 4 * hh;
-          u32x2 w;
-          w[0] = pack_bf16x2(o[qb][db][4 * rq] * inv, o[qb][db][4 * rq + 1] * inv);
-          w[1] = pack_bf16x2(o[qb][db][4 * rq + 2] * inv, o[qb][db][4 * rq + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
-        }
-      if (a.lse && hh == 0)
-        a.lse[bh * a.n + qpos[qb]] =
-            (l_tot > 0.f) ? (ref[qb] + __log2f(l_tot)) * kLn2 : neg_inf();
-    }
-  }
+  if (gi >= 0) body(std::integral_constant<int, kGlobalRows>{}, gi);
+  else body(std::integral_constant<int, MODE_MAIN>{}, mi);
 }
 
 // Merge the per-chunk partials of every global row and write its output and lse.
-// One wave per (batch, head, global row), four rows per workgroup; lane l owns output columns
-// l, l + 64, ...  The (m, l) pairs of a row are the same for every lane of its wave (scalar
-// loads); the partial outputs of consecutive chunks are independent loads.
-constexpr int kCombineRows = 4;
+// One 256-thread workgroup per (batch, head, global row).  Thread t owns output columns
+// 4(t % (D/4)) .. +3 of the chunks t / (D/4), + 256/(D/4), ...: every partial load of the row is
+// in flight at once.  Each thread merges its chunks against its own running maximum; the chunk
+// groups are then merged through LDS (one load round, one LDS round).
+constexpr int kCombineThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(64 * kCombineRows) void global_combine_kernel(FwdArgs a) {
-  const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs args) {
+  constexpr int QPR = D / 4;                    // column quads per row
+  constexpr int CG = kCombineThreads / QPR;     // chunk groups
+  constexpr float kNegInf = -__builtin_inff();
+  __shared__ float4 part[CG][QPR];
+  __shared__ float gmax[CG], gsum[CG];
+  const FwdCore a = args;
+  const int t = threadIdx.x;
   const long rows = (long)a.B * a.H * a.g;
-  const long row = (long)blockIdx.x * kCombineRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= rows) return;
+  const long row = blockIdx.x;
   const long bh = row / a.g;
   const int c = (int)(row - bh * a.g);
   const int b = (int)(bh / a.H);
   const int pos = a.gidx[(long)b * a.g + c];
-  if (pos < 0 || pos >= a.n) return;  // out-of-range global index: nothing to write
+  if (pos < 0 || pos >= a.n) return;  // out-of-range global index: nothing to write (uniform)
   const int K = a.chunks;
   const float* po = a.part + row * K * D;
   const float* pml = a.part + rows * K * D + row * K * 2;
-  constexpr float kNegInf = -__builtin_inff();
-  float M = kNegInf;
-  for (int k = 0; k < K; ++k) M = fmaxf(M, pml[2 * k]);
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  if (M != kNegInf) {
+  const int cg = t / QPR, cq = t % QPR;
+  float m = kNegInf, l = 0.f;                 // running max and normaliser of this thread
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-    for (int k = 0; k < K; ++k) {
-      const float mk = pml[2 * k];
-      const float w = (mk == kNegInf) ? 0.f : exp2f(mk - M);  // chunk's weights against M
-      L += w * pml[2 * k + 1];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * po[(long)k * D + lane + 64 * e];
+  for (int k = cg; k < K; k += CG) {
+    const float mk = pml[2 * k];
+    const float lk = pml[2 * k + 1];
+    const float4 v = *reinterpret_cast<const float4*>(po + (long)k * D + 4 * cq);
+    if (mk == kNegInf) continue;  // chunk with no key: o = 0, l = 0
+    const float mn = fmaxf(m, mk);
+    const float s_old = (m == kNegInf) ? 0.f : exp2f(m - mn), s_new = exp2f(mk - mn);
+    acc.x = acc.x * s_old + v.x * s_new;
+    acc.y = acc.y * s_old + v.y * s_new;
+    acc.z = acc.z * s_old + v.z * s_new;
+    acc.w = acc.w * s_old + v.w * s_new;
+    l = l * s_old + lk * s_new;
+    m = mn;
+  }
+  part[cg][cq] = acc;
+  if (cq == 0) {
+    gmax[cg] = m;
+    gsum[cg] = l;
+  }
+  __syncthreads();
+  if (t < QPR) {
+    float M = kNegInf;
+    for (int gi = 0; gi < CG; ++gi) M = fmaxf(M, gmax[gi]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+    if (M != kNegInf) {
+      for (int gi = 0; gi < CG; ++gi) {
+        if (gmax[gi] == kNegInf) continue;
+        const float w = exp2f(gmax[gi] - M);
+        const float4 v = part[gi][t];
+        o.x += w * v.x;
+        o.y += w * v.y;
+        o.z += w * v.z;
+        o.w += w * v.w;
+        L += w * gsum[gi];
+      }
     }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    uint16_t* orow = a.out + (bh * a.n + pos) * D + 4 * t;
+    orow[0] = __builtin_bit_cast(uint16_t, (__bf16)(o.x * inv));
+    orow[1] = __builtin_bit_cast(uint16_t, (__bf16)(o.y * inv));
+    orow[2] = __builtin_bit_cast(uint16_t, (__bf16)(o.z * inv));
+    orow[3] = __builtin_bit_cast(uint16_t, (__bf16)(o.w * inv));
+    if (a.lse && t == 0) a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  uint16_t* orow = a.out + (bh * a.n + pos) * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float v = acc[e] * inv;
-    orow[lane + 64 * e] = __builtin_bit_cast(uint16_t, (__bf16)v);
-  }
-  if (a.lse && lane == 0)
-    a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 template <int D, int NW, int QB, int MODE>
@@ -825,14 +890,15 @@ hipError_t launch_one(const FwdArgs& a, long grid, hipStream_t s) {
 
 }  // namespace
 
-// Query rows per workgroup of the main kernel: 128 in window mode (four waves of one 32-row
-// block), the block size in layout mode.
+// Query rows per workgroup of the main work: 128 in window mode (four waves of one 32-row
+// block), the block size in layout mode.  The global-row workgroups of the same launch take as
+// many global rows (one 32-row block per wave).
 int main_rows_per_workgroup(int mode, int d, int block) {
   (void)d;
   return mode == kLayout ? block : 128;
 }
 
-hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStream_t s) {
+hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s) {
   if (mode == kBand) {
     if (d == 64) return launch_one<64, 4, 1, kBand>(a, grid, s);
     if (d == 128) return launch_one<128, 4, 1, kBand>(a, grid, s);
@@ -848,25 +914,10 @@ hipError_t launch_mfma_main(const FwdArgs& a, int d, int mode, int grid, hipStre
   return hipErrorInvalidValue;
 }
 
-int global_rows_per_workgroup(int g) { return g <= 64 ? 64 : 128; }
-
-hipError_t launch_mfma_global_partial(const FwdArgs& a, int d, hipStream_t s) {
-  const int qt = global_rows_per_workgroup(a.g);
-  const long grid = (long)a.B * a.H * ((a.g + qt - 1) / qt) * a.chunks;
-  if (qt == 64) {
-    if (d == 64) return launch_one<64, 2, 1, kGlobalRows>(a, grid, s);
-    if (d == 128) return launch_one<128, 2, 1, kGlobalRows>(a, grid, s);
-  } else {
-    if (d == 64) return launch_one<64, 4, 1, kGlobalRows>(a, grid, s);
-    if (d == 128) return launch_one<128, 4, 1, kGlobalRows>(a, grid, s);
-  }
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.g;
   if (rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + kCombineRows - 1) / kCombineRows)), block(64 * kCombineRows);
+  const dim3 grid((unsigned)rows), block(kCombineThreads);
   if (d == 64) hipLaunchKernelGGL(global_combine_kernel<64>, grid, block, 0, s, a);
   else if (d == 128) hipLaunchKernelGGL(global_combine_kernel<128>, grid, block, 0, s, a);
   else return hipErrorInvalidValue;

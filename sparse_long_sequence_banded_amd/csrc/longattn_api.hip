@@ -145,14 +145,15 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P) {
     a.tiles_per_b = (int)per_b;
     p.grid_main = per_b * a.B;
     if (a.g > 0) {
+      // global rows: the same launch adds workgroups of qt global rows x kGlobalChunk keys
       a.chunks = (a.n + kGlobalChunk - 1) / kGlobalChunk;
-      const long gq = global_rows_per_workgroup(a.g);
-      const long grid_g = (long)a.B * a.H * ((a.g + gq - 1) / gq) * a.chunks;
-      if (grid_g > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
+      const long grid_g = (long)a.B * a.H * ((a.g + qt - 1) / qt) * a.chunks;
+      if (grid_g + p.grid_main > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
         return LONGATTN_ERR_UNSUPPORTED;
-      // partials (o, then m and l) followed by one int32 record per (batch, global column)
+      a.grid_rows = (int)grid_g;
+      // partial outputs, then their (m, l) pairs
       p.part_floats = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2);
-      p.ws_bytes = p.part_floats * sizeof(float) + (size_t)a.B * a.g * sizeof(int32_t);
+      p.ws_bytes = p.part_floats * sizeof(float);
     }
   } else if (for_forward) {
     if ((long)a.B * a.H * a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
@@ -243,24 +244,20 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   a.kpad = desc->key_pad;
   a.layout = desc->block_layout;
   a.part = static_cast<float*>(workspace);
-  a.gmeta = p.ws_bytes ? reinterpret_cast<int32_t*>(a.part + p.part_floats) : nullptr;
 
-  // bf16: global-row partials first (they also publish the global columns' positions and
-  // validity), then the main sparse kernel, then the global-row combine, which overwrites the
-  // rows of global tokens that the main kernel also produced.
+  // bf16: one launch computes every non-global row and, in extra workgroups, the global rows'
+  // per-chunk partials; the combine then writes the global rows (overwriting what the main work
+  // produced for them).
   hipError_t e = hipSuccess;
   if (!mark(0)) return LONGATTN_ERR_HIP;
   if (p.bf16) {
-    if (a.g > 0) e = launch_mfma_global_partial(a, desc->d, s);
+    e = launch_attention(a, desc->d, p.mode, p.grid_main + a.grid_rows, s);
     if (e != hipSuccess || !mark(1)) return LONGATTN_ERR_HIP;
-    e = launch_mfma_main(a, desc->d, p.mode, (int)p.grid_main, s);
-    if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
     if (a.g > 0) e = launch_global_combine(a, desc->d, s);
-    if (e != hipSuccess || !mark(3)) return LONGATTN_ERR_HIP;
+    if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
   } else {
-    if (!mark(1)) return LONGATTN_ERR_HIP;
     e = launch_rowwise_f32(a, desc->d, s);
-    if (e != hipSuccess || !mark(2) || !mark(3)) return LONGATTN_ERR_HIP;
+    if (e != hipSuccess || !mark(1) || !mark(2)) return LONGATTN_ERR_HIP;
   }
   return LONGATTN_OK;
 }
