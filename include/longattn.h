@@ -94,12 +94,13 @@ longattn_status longattn_forward(const longattn_desc* desc, const void* q, const
                                  const void* v, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
-/* The same pass, recording caller-created hipEvent_t handles on `stream` at its phase
- * boundaries so the caller can time each kernel: marks[0] before the attention kernel (every
- * non-global row plus the global rows' per-chunk partials, one launch), marks[1] after it,
- * marks[2] after the global-row combine kernel (equal to marks[1] when it does not run).
- * n_marks must be 0 (no marks, same as longattn_forward) or LONGATTN_N_MARKS. */
-#define LONGATTN_N_MARKS 3
+/* The same pass, with caller-created hipEvent_t handles that time each kernel: marks[0] and
+ * marks[1] record the start and end of the attention kernel (every non-global row plus the
+ * global rows' per-chunk partials, one launch), marks[2] and marks[3] those of the global-row
+ * combine kernel.  The events are attached to the kernels' own dispatches; when the combine does
+ * not run, marks[2] and marks[3] are recorded back to back on `stream` after the attention
+ * kernel.  n_marks must be 0 (no marks, same as longattn_forward) or LONGATTN_N_MARKS. */
+#define LONGATTN_N_MARKS 4
 longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
                                         const void* v, void* out, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream,

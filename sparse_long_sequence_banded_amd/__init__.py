@@ -26,7 +26,7 @@ LONGATTN_ERR_WORKSPACE = 4
 LONGATTN_ERR_HIP = 5
 LONGATTN_BF16 = 0
 LONGATTN_F32 = 1
-LONGATTN_N_MARKS = 3
+LONGATTN_N_MARKS = 4
 
 EXPORTED = (
     "longattn_workspace_size",

@@ -8,7 +8,7 @@ namespace longattn {
 
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
 constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
-constexpr int kGlobalChunk = 256;     // keys per global-row partial workgroup
+constexpr int kGlobalChunk = 1024;    // keys per global-row partial workgroup
 constexpr int kGlobalCap = 256;       // global tokens the bf16 kernels stage in LDS
 
 enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };
@@ -46,8 +46,14 @@ struct FwdArgs : FwdCore {
 
 // Launchers (defined next to their kernels).
 int main_rows_per_workgroup(int mode, int d, int block);
-hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s);
-hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s);
+// Optional events that record a kernel's own start and end (attached to its dispatch).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s,
+                            const LaunchEvents& ev);
+hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);
 

@@ -34,6 +34,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "attn_args.h"
 
 namespace longattn {
@@ -307,24 +309,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
         }
       }
     }
-    // Q fragments (B operands of the score MFMAs), loaded once.
-    const float c2 = a.scale_log2;
-    u32x4 qf[QB][KS];
-  #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        qf[qb][s] = u32x4{0, 0, 0, 0};
-        if (qpos[qb] >= 0)
-          qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
-      }
-    // Consume the fragments here so that the compiler waits for these loads before the tile loop;
-    // otherwise it waits for them (vmcnt(0), which also drains the K/V prefetch) inside the loop.
-  #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
-
     // ------------------------------------------------------------------ key tiles
     int n_local = 0, k_lo = 0, k_hi = -1, tpb = 1;
     if constexpr (MODE == kBand) {
@@ -385,6 +369,59 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
       }
       return T;
     };
+
+    // ------------------------------------------------------------------ tile loading
+    // Wave w moves the 1 KB blocks w*LPW .. w*LPW + LPW - 1 of a tile: all of one matrix (K for
+    // the first half of the waves, the "K waves", V for the rest).  Block `sub` of a matrix holds
+    // rows RPB*sub .. RPB*sub + RPB - 1; lane l moves row RPB*sub + l/CH, 16-byte chunk l%CH, to
+    // LDS byte sub*1024 + 16*l (the chunk's swizzled slot in that row).
+    const int mat = (wave * LPW) / CH;
+    const int sub0 = (wave * LPW) % CH;
+    auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
+    auto ld_col = [&](int j) -> int {
+      const int row = ld_row(j);
+      return 8 * ((lane % CH) ^ (mat == 0 ? swz_k<D>(row) : swz_v<D>(row)));
+    };
+    // byte offsets of this lane's chunks within a local tile starting at row 0 (rows past the
+    // sequence end land at or beyond the resource size, so they read zeros)
+    uint32_t voff[LPW];
+  #pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
+    const uint16_t* msrc = (mat == 0) ? Kb : Vb;
+    auto issue = [&](unsigned char* st, const Tile& T) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + sub0 * 1024));
+      if (kHasGlobalCols && T.gathered) {
+        const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
+  #pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const int pos = g_pos[T.base + min(ld_row(j), T.count - 1)];
+          lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
+        }
+      } else {
+        const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
+  #pragma unroll
+        for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
+      }
+    };
+    const bool kwave = mat == 0;
+    // The first NS-1 tiles' loads go out first when they are local tiles (they need nothing from
+    // the staging below), so their latency overlaps that of the Q fragments and the staging.
+  #pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < n_local) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
+
+    // Q fragments (B operands of the score MFMAs), loaded once.
+    const float c2 = a.scale_log2;
+    u32x4 qf[QB][KS];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        qf[qb][s] = u32x4{0, 0, 0, 0};
+        if (qpos[qb] >= 0)
+          qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
+      }
 
     // ------------------------------------------------------------------ staging in LDS
     // Global-key columns: position and validity, once per workgroup.  A usable global key is
@@ -455,42 +492,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
         }
       }
     }
+    // Consume the fragments here so that the compiler waits for these loads before the tile loop;
+    // otherwise it waits for them (vmcnt(0), which also drains the K/V prefetch) inside the loop.
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
     __syncthreads();
+    // gathered tiles among the first NS-1 (their rows come from the staged positions)
+  #pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i >= n_local && i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
 
-    // ------------------------------------------------------------------ tile loading
-    // Wave w moves the 1 KB blocks w*LPW .. w*LPW + LPW - 1 of a tile: all of one matrix (K for
-    // the first half of the waves, the "K waves", V for the rest).  Block `sub` of a matrix holds
-    // rows RPB*sub .. RPB*sub + RPB - 1; lane l moves row RPB*sub + l/CH, 16-byte chunk l%CH, to
-    // LDS byte sub*1024 + 16*l (the chunk's swizzled slot in that row).
-    const int mat = (wave * LPW) / CH;
-    const int sub0 = (wave * LPW) % CH;
-    auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
-    auto ld_col = [&](int j) -> int {
-      const int row = ld_row(j);
-      return 8 * ((lane % CH) ^ (mat == 0 ? swz_k<D>(row) : swz_v<D>(row)));
-    };
-    // byte offsets of this lane's chunks within a local tile starting at row 0 (rows past the
-    // sequence end land at or beyond the resource size, so they read zeros)
-    uint32_t voff[LPW];
-  #pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
-    const uint16_t* msrc = (mat == 0) ? Kb : Vb;
-    auto issue = [&](unsigned char* st, const Tile& T) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(st + sub0 * 1024));
-      if (kHasGlobalCols && T.gathered) {
-        const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
-  #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-          const int pos = g_pos[T.base + min(ld_row(j), T.count - 1)];
-          lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
-        }
-      } else {
-        const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
-  #pragma unroll
-        for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
-      }
-    };
+
     // window mode: bits of the usable global keys among the rows of local tile t
     auto global_keys = [&](const Tile& T, int t) -> unsigned long long {
       if (n_gtiles == 0) return 0ull;
@@ -729,12 +743,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     // t+1 .. t+NS-1 stream into the others.  At the top of step t each wave waits for its own
     // loads of tile t (later tiles' loads stay in flight: loads complete in issue order), then the
     // barrier makes tile t visible to every wave and retires every read of stage (t-1) % NS, which
-    // is refilled with tile t+NS-1 right after.
-    const bool kwave = mat == 0;
+    // is refilled with tile t+NS-1 right after.  Tiles 0 .. NS-2 were issued above.
     if (n_tiles > 0) {
-  #pragma unroll
-      for (int i = 0; i < NS - 1; ++i)
-        if (i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
       int st = 0;  // stage of tile t
       for (int t = 0; t < n_tiles; ++t) {
         if (NS == 3 && t + 1 < n_tiles) wait_vmcnt<LPW>();
@@ -881,10 +891,14 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
 }
 
 template <int D, int NW, int QB, int MODE>
-hipError_t launch_one(const FwdArgs& a, long grid, hipStream_t s) {
+hipError_t launch_one(const FwdArgs& a, long grid, hipStream_t s, const LaunchEvents& ev) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MODE>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     s, a);
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MODE>), dim3((unsigned)grid),
+                          dim3(NW * 64), 0, s, ev.start, ev.stop, 0, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MODE>), dim3((unsigned)grid), dim3(NW * 64),
+                       0, s, a);
   return hipGetLastError();
 }
 
@@ -898,28 +912,35 @@ int main_rows_per_workgroup(int mode, int d, int block) {
   return mode == kLayout ? block : 128;
 }
 
-hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s) {
+hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s,
+                            const LaunchEvents& ev) {
   if (mode == kBand) {
-    if (d == 64) return launch_one<64, 4, 1, kBand>(a, grid, s);
-    if (d == 128) return launch_one<128, 4, 1, kBand>(a, grid, s);
+    if (d == 64) return launch_one<64, 4, 1, kBand>(a, grid, s, ev);
+    if (d == 128) return launch_one<128, 4, 1, kBand>(a, grid, s, ev);
   } else if (mode == kLayout) {
     if (a.block == 64) {
-      if (d == 64) return launch_one<64, 2, 1, kLayout>(a, grid, s);
-      if (d == 128) return launch_one<128, 2, 1, kLayout>(a, grid, s);
+      if (d == 64) return launch_one<64, 2, 1, kLayout>(a, grid, s, ev);
+      if (d == 128) return launch_one<128, 2, 1, kLayout>(a, grid, s, ev);
     } else if (a.block == 128) {
-      if (d == 64) return launch_one<64, 4, 1, kLayout>(a, grid, s);
-      if (d == 128) return launch_one<128, 4, 1, kLayout>(a, grid, s);
+      if (d == 64) return launch_one<64, 4, 1, kLayout>(a, grid, s, ev);
+      if (d == 128) return launch_one<128, 4, 1, kLayout>(a, grid, s, ev);
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s) {
+hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s, const LaunchEvents& ev) {
   const long rows = (long)a.B * a.H * a.g;
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kCombineThreads);
-  if (d == 64) hipLaunchKernelGGL(global_combine_kernel<64>, grid, block, 0, s, a);
-  else if (d == 128) hipLaunchKernelGGL(global_combine_kernel<128>, grid, block, 0, s, a);
+  auto launch = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, a);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+  };
+  if (d == 64) launch(global_combine_kernel<64>);
+  else if (d == 128) launch(global_combine_kernel<128>);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -217,9 +217,10 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   longattn_status st = plan_call(desc, true, &p);
   if (st != LONGATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> bool {
-    return !n_marks || hipEventRecord(reinterpret_cast<hipEvent_t>(marks[i]), s) == hipSuccess;
+  auto ev = [&](int i) -> hipEvent_t {
+    return n_marks ? reinterpret_cast<hipEvent_t>(marks[i]) : nullptr;
   };
+  auto mark = [&](int i) -> bool { return !n_marks || hipEventRecord(ev(i), s) == hipSuccess; };
   if (p.empty) {
     for (int i = 0; i < n_marks; ++i)
       if (!mark(i)) return LONGATTN_ERR_HIP;
@@ -247,17 +248,22 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
 
   // bf16: one launch computes every non-global row and, in extra workgroups, the global rows'
   // per-chunk partials; the combine then writes the global rows (overwriting what the main work
-  // produced for them).
+  // produced for them).  Marks are attached to the kernels' own dispatches, so they time the
+  // kernels themselves.
   hipError_t e = hipSuccess;
-  if (!mark(0)) return LONGATTN_ERR_HIP;
   if (p.bf16) {
-    e = launch_attention(a, desc->d, p.mode, p.grid_main + a.grid_rows, s);
-    if (e != hipSuccess || !mark(1)) return LONGATTN_ERR_HIP;
-    if (a.g > 0) e = launch_global_combine(a, desc->d, s);
-    if (e != hipSuccess || !mark(2)) return LONGATTN_ERR_HIP;
+    e = launch_attention(a, desc->d, p.mode, p.grid_main + a.grid_rows, s, {ev(0), ev(1)});
+    if (e != hipSuccess) return LONGATTN_ERR_HIP;
+    if (a.g > 0) {
+      e = launch_global_combine(a, desc->d, s, {ev(2), ev(3)});
+      if (e != hipSuccess) return LONGATTN_ERR_HIP;
+    } else if (!mark(2) || !mark(3)) {
+      return LONGATTN_ERR_HIP;
+    }
   } else {
+    if (!mark(0)) return LONGATTN_ERR_HIP;
     e = launch_rowwise_f32(a, desc->d, s);
-    if (e != hipSuccess || !mark(1) || !mark(2)) return LONGATTN_ERR_HIP;
+    if (e != hipSuccess || !mark(1) || !mark(2) || !mark(3)) return LONGATTN_ERR_HIP;
   }
   return LONGATTN_OK;
 }

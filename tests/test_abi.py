@@ -117,9 +117,12 @@ def test_pointer_alignment_and_workspace_checks():
 
 
 def test_workspace_size_formula():
-    # global-row partials: B*H*g*chunks*(d+2) floats (chunks of 256 keys: 1000 keys -> 4)
+    # global-row partials: B*H*g*chunks*(d+2) floats (chunks of 1024 keys: 1000 keys -> 1,
+    # 3000 keys -> 3)
     dg = _desc(batch=2, heads=3, n=1000, d=128, n_global=5, global_idx=FAKE)
-    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 4 * 130 * 4)
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 1 * 130 * 4)
+    dg = _desc(batch=2, heads=3, n=3000, d=64, n_global=5, global_idx=FAKE)
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 3 * 66 * 4)
     assert la.longattn_workspace_size(_desc()) == (la.LONGATTN_OK, 0)
     f32 = _desc(dtype=la.LONGATTN_F32, n_global=5, global_idx=FAKE)
     assert la.longattn_workspace_size(f32) == (la.LONGATTN_OK, 0)

@@ -207,5 +207,5 @@ def test_marks_time_each_phase():
     la.forward(t["q"], t["k"], t["v"], scale=inp.scale, win_left=256, win_right=256,
                global_idx=t["global_idx"], key_pad=t["key_pad"], marks=handles)
     torch.cuda.synchronize()
-    spans = [ev[i].elapsed_time(ev[i + 1]) for i in range(la.LONGATTN_N_MARKS - 1)]
-    assert all(s >= 0 for s in spans) and spans[0] > 0 and spans[1] > 0  # attention, combine
+    spans = [ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])]  # attention, combine
+    assert all(s > 0 for s in spans) and ev[1].elapsed_time(ev[2]) >= 0
