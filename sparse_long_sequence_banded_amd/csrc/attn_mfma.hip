@@ -115,7 +115,7 @@ struct Tile {
 };
 
 // LDS stages of K tiles and of V tiles: two each (loads run one tile ahead).  At head dim 64 a
-// workgroup then needs about 34 KB of LDS, so four fit on a CU (more resident waves measured
+// workgroup then needs about 36 KB of LDS, so four fit on a CU (more resident waves measured
 // faster than a third stage).
 template <int D>
 constexpr int kStages = 2;
@@ -225,13 +225,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     constexpr int DB = D / 32;         // 32-row blocks of O^T
     constexpr int MAT = kKeyTile * D * 2;
     constexpr int NS = kStages<D>;
-    static_assert(NS == 2 || NS == 3, "stage count");
+    static_assert(NS == 2, "the tile schedule below uses two stages");
     constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
     constexpr int LPW = NLOAD / NW;    // of which each wave issues
     constexpr int RPB = 64 / CH;       // rows per 1 KB block
-    constexpr int GREG = kGlobalCap / NT;
+    constexpr int GREG = (kGlobalCap + NT - 1) / NT;
     static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
-    static_assert(kGlobalCap % NT == 0, "global staging must split evenly");
+    static_assert(kGlobalCap % 64 == 0 && NT % 64 == 0, "global staging works in whole waves");
     constexpr bool kHasGlobalCols = MODE != kGlobalRows;
 
     auto& stage_k = sm.stage_k;
@@ -405,8 +405,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
       }
     };
     const bool kwave = mat == 0;
-    // The first NS-1 tiles' loads go out first when they are local tiles (they need nothing from
-    // the staging below), so their latency overlaps that of the Q fragments and the staging.
+    // Global column positions are loaded first (the staging below needs them and, with key
+    // padding, loads a pad byte at each), then the first NS-1 tiles' loads go out when they are
+    // local tiles (they need nothing from the staging), so their latency overlaps that of the Q
+    // fragments and the staging.
+    int gx[GREG];
+    if constexpr (kHasGlobalCols) {
+  #pragma unroll
+      for (int i = 0; i < GREG; ++i) {
+        const int c = tid + NT * i;
+        gx[i] = (n_gtiles > 0 && c < a.g) ? gb[c] : a.n;
+      }
+    }
   #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
       if (i < n_local) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
@@ -441,7 +451,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
         for (int i = 0; i < GREG; ++i) {
           const int c = tid + NT * i;
-          const int x = (c < a.g) ? gb[c] : a.n;
+          if (NT * (i + 1) > kGlobalCap && c >= kGlobalCap) continue;  // whole waves past the cap
+          const int x = gx[i];
           bool ok = x >= 0 && x < a.n;         // a usable key: in range and not padded
           if (ok && pad) ok = pad[x] == 0;
           const int pos = min(max(x, 0), a.n);  // keeps the positions ascending
@@ -484,11 +495,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
       pad_staged = words <= kPadWords;
       pad_lo = (int)lo;
       if (pad_staged) {
-        for (int w = wave; w < (int)words; w += NW) {
-          const int pos = pad_lo + 64 * w + lane;
-          const bool ok = pos < a.n && pad[pos] == 0;
-          const unsigned long long m = __ballot(ok);
-          if (lane == 0) pad_bits[w] = m;
+        // four words per wave per round, their loads issued together
+        for (int w0 = wave; w0 < (int)words; w0 += 4 * NW) {
+          int pb[4];
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int pos = pad_lo + 64 * (w0 + NW * u) + lane;
+            pb[u] = (w0 + NW * u < (int)words && pos < a.n) ? pad[pos] : 1;
+          }
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const unsigned long long m = __ballot(pb[u] == 0);
+            if (lane == 0 && w0 + NW * u < (int)words) pad_bits[w0 + NW * u] = m;
+          }
         }
       }
     }
@@ -739,19 +758,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     };
 
     // ------------------------------------------------------------------ tile loop
-    // NS LDS stages of K tiles and NS of V tiles; tile t lives in stage t % NS while tiles
-    // t+1 .. t+NS-1 stream into the others.  At the top of step t each wave waits for its own
-    // loads of tile t (later tiles' loads stay in flight: loads complete in issue order), then the
-    // barrier makes tile t visible to every wave and retires every read of stage (t-1) % NS, which
-    // is refilled with tile t+NS-1 right after.  Tiles 0 .. NS-2 were issued above.
+    // Two LDS stages of K tiles and two of V tiles; tile t lives in stage t % 2.  Step t: a
+    // barrier retires every read of tile t-1, whose stage then takes tile t+1's loads; each wave
+    // then waits for its own loads of tile t only (tile t+1's stay in flight: loads complete in
+    // issue order), and a second barrier makes tile t visible to every wave.  Issuing tile t+1
+    // before waiting for tile t keeps two tiles in flight whenever a load is late.  Tile 0 was
+    // issued above.
     if (n_tiles > 0) {
       int st = 0;  // stage of tile t
       for (int t = 0; t < n_tiles; ++t) {
-        if (NS == 3 && t + 1 < n_tiles) wait_vmcnt<LPW>();
+        if (t > 0) __syncthreads();  // every wave is done with tile t-1: its stage may be refilled
+        if (t + 1 < n_tiles) issue(kwave ? stage_k[st ^ 1] : stage_v[st ^ 1], tile_of(t + 1));
+        if (t + 1 < n_tiles) wait_vmcnt<LPW>();  // tile t landed; tile t+1 stays in flight
         else wait_vmcnt<0>();
-        __syncthreads();
-        const int stp = (st == 0) ? NS - 1 : st - 1;  // stage of tile t-1 (= that of t+NS-1)
-        if (t + NS - 1 < n_tiles) issue(kwave ? stage_k[stp] : stage_v[stp], tile_of(t + NS - 1));
+        __syncthreads();  // tile t visible to every wave
         const Tile T = tile_of(t);
         bool need_band = false;
         if (reach(T, need_band)) {
@@ -763,7 +783,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
           scores(stage_k[st], sc);
           finish(sc, stage_v[st], T, vmask, need_band);
         }
-        st = (st + 1 == NS) ? 0 : st + 1;
+        st ^= 1;
       }
     }
 
