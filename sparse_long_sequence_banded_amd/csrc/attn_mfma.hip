@@ -53,6 +53,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRescaleLog2 = 8.f;  // move the row's reference only when its max exceeds it by > 2^8
+constexpr float kFastWeightSum = 65536.f;  // fast path: a lane's 16 weights of a half sum to <= 2^16
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -650,77 +651,88 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
         }
       }
 
-      // ---- online softmax step over the 64 keys.  Weights are 2^(c2 s - ref), c2 = scale *
-      // log2(e).  ref only moves when a row sees its first allowed key (then ref := that tile's row
-      // max) or when a row's max exceeds ref by more than 2^8; otherwise every weight stays below
-      // 2^8, which fp32 and bf16 hold without loss, and the final normalisation by l makes the
-      // result exact.  In the common case no row moves: each weight is one FMA and one exp2.
-      float xm[QB];
-      bool need[QB];
-      bool need_any = false;
-  #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const f32x16& u = sc[0][qb];
-        const f32x16& v = sc[1][qb];
-        float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
-        float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), u[15]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[0]), v[1]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[2]), v[3]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[4]), v[5]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[6]), v[7]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[8]), v[9]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[10]), v[11]);
-        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, v[12]), v[13]);
-        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, v[14]), __builtin_fmaxf(x1, v[15]));
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
-                                                         false, false);
-        const float x = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
-        xm[qb] = x;
-        need[qb] = (x != neg_inf()) & (!has[qb] | (x - ref[qb] > kRescaleLog2));
-        need_any = need_any | need[qb];
-      }
-      if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
-        // some row moves its reference (rare): per lane, the new reference is the row max if the
-        // row moves, else the old one
-  #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float nref = need[qb] ? xm[qb] : ref[qb];
-          const float alpha = has[qb] ? exp2_fast(ref[qb] - nref) : 1.f;  // old weights rescaled
-          ref[qb] = nref;
-          has[qb] = has[qb] || need[qb];
-          l_run[qb] *= alpha;
-  #pragma unroll
-          for (int db = 0; db < DB; ++db)
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        }
-      }
-
+      // ---- online softmax step, one 32-key half at a time.  Weights are 2^(c2 s - ref), c2 =
+      // scale * log2(e), against a per-row reference ref; the final normalisation by l makes the
+      // result exact for any reference that keeps the weights finite and not all underflowing.
+      // Fast path (rows that already have a reference): exponentiate against it without a row
+      // max and accept when every lane's 16 weights sum to at most 2^16 (so no weight exceeds
+      // 2^16 and nothing overflows).  Otherwise (a row's first allowed key, or a score far above
+      // the reference) take the half's row max: a row moves its reference to that max when it
+      // has none yet or when the max exceeds ref by more than 2^8, and the weights are redone.
   #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t pk[QB][8];
+        float part[QB];
+        auto exponentiate = [&]() {
   #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float nr = -ref[qb];
-          float la = 0.f, lb = 0.f;
+          for (int qb = 0; qb < QB; ++qb) {
+            const float nr = -ref[qb];
+            float la = 0.f, lb = 0.f;
   #pragma unroll
-          for (int r = 0; r < 16; r += 4) {
-            const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
-            const float p1 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 1], c2, nr));
-            const float p2 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 2], c2, nr));
-            const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
-            pk[qb][r >> 1] = pack_bf16x2(p0, p1);
-            pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
-            la += p0 + p1;
-            lb += p2 + p3;
+            for (int r = 0; r < 16; r += 4) {
+              const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
+              const float p1 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 1], c2, nr));
+              const float p2 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 2], c2, nr));
+              const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
+              pk[qb][r >> 1] = pack_bf16x2(p0, p1);
+              pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
+              la += p0 + p1;
+              lb += p2 + p3;
+            }
+            part[qb] = la + lb;
           }
-          l_run[qb] += la + lb;
+        };
+        bool no_ref = false;
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) no_ref = no_ref | !has[qb];
+        bool slow = __builtin_amdgcn_ballot_w64(no_ref) != 0ull;
+        if (!slow) {
+          exponentiate();
+          bool over = false;
+  #pragma unroll
+          for (int qb = 0; qb < QB; ++qb) over = over | !(part[qb] <= kFastWeightSum);
+          slow = __builtin_amdgcn_ballot_w64(over) != 0ull;
         }
+        if (slow) {
+          float xm[QB];
+          bool need[QB];
+          bool need_any = false;
+  #pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const f32x16& u = sc[kb][qb];
+            float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
+            float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
+            x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
+            x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
+            x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
+            x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
+            x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), __builtin_fmaxf(x1, u[15]));
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0),
+                                                             __float_as_uint(x0), false, false);
+            const float x = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+            xm[qb] = x;
+            need[qb] = (x != neg_inf()) & (!has[qb] | (x - ref[qb] > kRescaleLog2));
+            need_any = need_any | need[qb];
+          }
+          if (__builtin_amdgcn_ballot_w64(need_any) != 0ull) {
+            // per lane, the new reference is the row max if the row moves, else the old one
+  #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              const float nref = need[qb] ? xm[qb] : ref[qb];
+              const float alpha = has[qb] ? exp2_fast(ref[qb] - nref) : 1.f;  // old weights
+              ref[qb] = nref;
+              has[qb] = has[qb] || need[qb];
+              l_run[qb] *= alpha;
+  #pragma unroll
+              for (int db = 0; db < DB; ++db)
+  #pragma unroll
+                for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+            }
+          }
+          exponentiate();
+        }
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
         // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
   #pragma unroll
         for (int gh = 0; gh < 2; ++gh) {
