@@ -79,12 +79,24 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: these calls fail validati
     (dict(block_layout=FAKE, block=32, max_kb=2, win_left=-1, win_right=-1),
      la.LONGATTN_ERR_UNSUPPORTED),
     (dict(n=(1 << 28) + 64), la.LONGATTN_ERR_UNSUPPORTED),
+    # bf16 limits: a head's K or V must stay under 2 GiB (32-bit buffer offsets) ...
+    (dict(n=1 << 23, d=128), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(n=1 << 24, d=64), la.LONGATTN_ERR_UNSUPPORTED),
+    # ... and at most 256 global tokens are staged per workgroup
+    (dict(n=4096, n_global=257, global_idx=FAKE), la.LONGATTN_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptors_are_rejected(kw, status):
     d = _desc(**kw)
     st, _ = la.longattn_workspace_size(d)
     assert st == status
     assert la.longattn_forward(d, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == status
+
+
+def test_largest_supported_sizes_are_accepted():
+    # just under the bf16 limits: n*d*2 = 2^31 - 256 bytes per head, 256 global tokens
+    assert la.longattn_workspace_size(_desc(n=(1 << 23) - 1, d=128))[0] == la.LONGATTN_OK
+    st, nbytes = la.longattn_workspace_size(_desc(n=8192, n_global=256, global_idx=FAKE))
+    assert st == la.LONGATTN_OK and nbytes > 0
 
 
 def test_bad_dilations_are_rejected():
