@@ -1,6 +1,7 @@
 """Benchmark: useful TFLOP/s of the banded sparse attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --decode swa512_decode_32k [--steps K] [--warmup W]
 
 One step is one full forward pass (global-row partials, main sparse kernel, global-row combine)
 over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
@@ -36,6 +37,9 @@ def _parse():
     ap.add_argument("--cpu-budget-gflop", type=float, default=640.0,
                     help="fp64 work of the oracle sample: whole heads (at least one); a workload "
                          "smaller than the budget is run repeatedly")
+    ap.add_argument("--decode", default=None, metavar="NAME",
+                    help="instead of the forward bench: time decode steps of the named decode "
+                         "workload (swa512_decode_32k), an HBM-bound path, reported in GB/s")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the attention bench: time K device-to-device copies of this "
                          "many MiB (a kernel of known HBM traffic, used to calibrate the "
@@ -60,6 +64,99 @@ def _copy_calibration(args):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": args.steps,
                       "ms_per_copy": round(dt * 1e3, 5),
                       "GB_per_s": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+
+
+def _decode_bench(args):
+    """Decode steps over a rolling or linear key/value cache: whole-step throughput in GB/s of
+    algorithmic bytes (each reachable K and V row read once, Q read, out and lse written)."""
+    import numpy as np
+    import torch
+
+    import sparse_long_sequence_banded_amd as la
+    from workloads.decode import DECODE_WORKLOADS, decode_to_torch, decode_workload_inputs
+
+    wl = DECODE_WORKLOADS[args.decode]
+    inp = decode_workload_inputs(wl)
+    dev = torch.device("cuda:0")
+    t = decode_to_torch(inp, dev)
+    q = t["q"]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    desc = la.make_decode_desc(q, t["k_cache"], t["positions"], window=inp.window,
+                               scale=inp.scale, ring=inp.ring)
+    _, ws_bytes = la.longattn_decode_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ptrs = (q.data_ptr(), t["k_cache"].data_ptr(), t["v_cache"].data_ptr(), out.data_ptr(),
+            lse.data_ptr(), ws.data_ptr(), ws_bytes, stream.cuda_stream)
+
+    def step():
+        st = la.longattn_decode(desc, *ptrs)
+        if st != la.LONGATTN_OK:
+            raise la.LongAttnError(st, "longattn_decode")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    elem = 2 if inp.dtype == "bf16" else 4
+    last = inp.positions.astype(np.int64) + inp.m - 1
+    first = np.maximum(0, inp.positions.astype(np.int64) - inp.window + 1)
+    rows_kv = int((last - first + 1).sum()) * inp.heads  # distinct K (and V) rows read
+    alg_bytes = (2 * rows_kv * inp.d * elem                           # K and V
+                 + 2 * inp.batch * inp.heads * inp.m * inp.d * elem  # q in, out
+                 + 4 * inp.batch * inp.heads * inp.m)                # lse
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": "decode step HBM throughput (K/V window rows read once + q, out, lse)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": inp.batch, "heads": inp.heads, "head_dim": inp.d,
+                   "window": inp.window, "new_rows": inp.m, "cache_len": inp.cache_len,
+                   "ring": inp.ring, "algorithmic_bytes": alg_bytes, "description": wl.note},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_window_kernel (whole step: one launch for this shape)",
+            "achieved": round(value, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        # whole decode steps (every sample) repeated for about 10 s
+        reps = 0
+        t0 = time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            oracle.decode_inputs(inp, nthreads=threads)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        rec["cpu_baseline"] = {
+            "value": round(alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole step ({inp.batch} samples, oracle forward on each gathered "
+                      f"window), {dt:.2f} s per step, mean of {reps}"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
 
 
 def _source_hash():
@@ -120,6 +217,9 @@ def main():
 
     if args.copy_calibration_mib:
         _copy_calibration(args)
+        return
+    if args.decode:
+        _decode_bench(args)
         return
 
     import numpy as np

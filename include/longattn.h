@@ -113,6 +113,49 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
 longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entries_out,
                                        void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Sliding-window decode over a key/value cache.
+ *
+ * The incremental form of the causal sliding window used by the SWA decoder layers (SWAN-GPT
+ * summary, section on the SWA-RoPE layers; SWA/Hybrid-RoPE blog, section 3: a 512-key window
+ * and a cost of O(n*w) because each token looks at its last w keys only).  Sample b brings m new
+ * query rows at absolute positions t0_b, t0_b + 1, ..., t0_b + m - 1; the row at position t
+ * attends the keys at positions max(0, t - window + 1) .. t, which must already be in the cache:
+ *
+ *   out[b,h,j] = sum_{p in P(t)} softmax_p(scale * q[b,h,j] . k(p)) * v(p),   t = t0_b + j,
+ *   lse[b,h,j] = log sum_{p in P(t)} exp(scale * q[b,h,j] . k(p)),
+ *
+ * which is exactly the forward pass above with win_left = window - 1, win_right = 0, no global
+ * tokens and no padding, restricted to those rows.  Position p lives in cache slot
+ *   p                  (linear cache, ring = 0; requires t0_b + m - 1 < cache_len), or
+ *   p mod cache_len    (rolling buffer, ring = 1; requires window + m - 1 <= cache_len so the
+ *                      slots of every needed position still hold it).
+ *
+ * q: DEVICE [B][H][m][d]; k_cache, v_cache: DEVICE [B][H][cache_len][d]; out: DEVICE
+ * [B][H][m][d]; lse: DEVICE fp32 [B][H][m] or NULL; positions: DEVICE int32 [B] (t0_b >= 0, read
+ * by the kernels; values that break the cache requirement above give keys outside the cache
+ * window no weight but are not otherwise reported unless LONGATTN_DEBUG=1).  bf16 and fp32,
+ * 1 <= d <= 256 with d % 8 == 0, 1 <= m <= 16.  Same alignment and error rules as
+ * longattn_forward.  The workspace holds per-chunk partial results when the library splits a
+ * window over several workgroups; its size depends on the shape (0 when one workgroup covers
+ * each window; then it may be NULL), so ask longattn_decode_workspace_size.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch, heads, d;
+  int32_t dtype;               /* longattn_dtype of q, the caches and out                      */
+  float scale;                 /* > 0 and finite                                                 */
+  int32_t window;              /* keys per row, >= 1 (the row itself and window - 1 before it)  */
+  int32_t n_queries;           /* m, new rows per sample                                         */
+  int32_t cache_len;           /* slots per (b, h) in the caches                                 */
+  int32_t ring;                /* 0: linear cache, 1: rolling buffer                             */
+  const int32_t* positions;    /* DEVICE [batch]: position of each sample's first new row        */
+} longattn_decode_desc;
+
+longattn_status longattn_decode_workspace_size(const longattn_decode_desc* desc, size_t* bytes);
+longattn_status longattn_decode(const longattn_decode_desc* desc, const void* q,
+                                const void* k_cache, const void* v_cache, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* longattn_status_string(longattn_status status);
 

@@ -6,7 +6,8 @@ CPU-baseline leg import this package.  It shares no code with the HIP library
 use is the seeded input generator package ``workloads``.
 
 The arithmetic lives in ``longattn_oracle.c`` (plain C, fp64, OpenMP); what it computes and
-which passage each step follows is written at the top of that file.  Every function is pinned
+which passage each step follows is written at the top of that file.  ``decode_inputs`` states a
+decode step over a key/value cache as that same forward pass on the gathered window.  Every function is pinned
 by the CPU tests (dense brute force, library full/causal attention, the Big Bird worked window
 example, closed-form counts and invariants); none is left "parity unpinned".
 """
@@ -183,3 +184,30 @@ def count_inputs(inp, nthreads: int = 0) -> int:
     return count(inp.batch, inp.heads, inp.n, win_left=inp.win_left, win_right=inp.win_right,
                  dilation=inp.dilation, global_idx=inp.global_idx, key_pad=inp.key_pad,
                  layout=inp.layout, block=inp.block, max_kb=inp.max_kb, nthreads=nthreads)
+
+
+def decode_inputs(inp, samples=None, nthreads: int = 0):
+    """Expected result of a sliding-window decode step on a ``workloads.decode.DecodeInputs``.
+
+    A decode step is the causal sliding-window forward pass (win_left = window - 1,
+    win_right = 0) restricted to the new rows.  For sample b the positions p0 .. last
+    (p0 = max(0, t0 - window + 1), last = t0 + m - 1) are taken from the cache in position order,
+    the new query rows go at the end of that sequence, and ``forward`` runs on it; its last m
+    rows are the step's result.  The window depends only on position differences (and the start
+    of the sequence stays at index 0 whenever p0 = 0), so each new row sees exactly the keys it
+    sees in the full sequence.  Returns (out [B', H, m, d], lse [B', H, m]) in fp64 for the listed
+    samples (all by default).
+    """
+    samples = range(inp.batch) if samples is None else list(samples)
+    outs, lses = [], []
+    q = inp.f64("q")
+    for b in samples:
+        _, k, v = inp.gathered(b)
+        L = k.shape[1]
+        qs = np.zeros_like(k)
+        qs[:, L - inp.m:] = q[b]
+        o, l, _ = forward(qs[None], k[None], v[None], scale=inp.scale,
+                          win_left=inp.window - 1, win_right=0, nthreads=nthreads)
+        outs.append(o[0, :, L - inp.m:])
+        lses.append(l[0, :, L - inp.m:])
+    return np.stack(outs), np.stack(lses)

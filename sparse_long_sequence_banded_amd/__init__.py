@@ -6,8 +6,9 @@ library's HIP kernels.  PyTorch supplies device memory and the current HIP strea
 library has not been built, every call raises ``LongAttnNotBuilt``; there is no fallback.
 
 The C entry points keep their names here (``longattn_forward``, ``longattn_workspace_size``,
-``longattn_forward_marked``, ``longattn_count_entries``, ``longattn_status_string``); the
-``forward`` / ``count_entries`` helpers wrap them for torch tensors.
+``longattn_forward_marked``, ``longattn_count_entries``, ``longattn_decode``,
+``longattn_decode_workspace_size``, ``longattn_status_string``); the ``forward`` /
+``count_entries`` / ``decode`` helpers wrap them for torch tensors.
 """
 
 import ctypes
@@ -33,6 +34,8 @@ EXPORTED = (
     "longattn_forward",
     "longattn_forward_marked",
     "longattn_count_entries",
+    "longattn_decode_workspace_size",
+    "longattn_decode",
     "longattn_status_string",
 )
 
@@ -56,6 +59,23 @@ class longattn_desc(ctypes.Structure):
         ("block_layout", ctypes.c_void_p),
         ("block", ctypes.c_int32),
         ("max_kb", ctypes.c_int32),
+    ]
+
+
+class longattn_decode_desc(ctypes.Structure):
+    """Mirror of ``struct longattn_decode_desc`` in include/longattn.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("n_queries", ctypes.c_int32),
+        ("cache_len", ctypes.c_int32),
+        ("ring", ctypes.c_int32),
+        ("positions", ctypes.c_void_p),
     ]
 
 
@@ -94,6 +114,11 @@ def load():
             lib.longattn_forward_marked.restype = ctypes.c_int
             lib.longattn_count_entries.argtypes = [D, P, P]
             lib.longattn_count_entries.restype = ctypes.c_int
+            DD = ctypes.POINTER(longattn_decode_desc)
+            lib.longattn_decode_workspace_size.argtypes = [DD, ctypes.POINTER(ctypes.c_size_t)]
+            lib.longattn_decode_workspace_size.restype = ctypes.c_int
+            lib.longattn_decode.argtypes = [DD, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.longattn_decode.restype = ctypes.c_int
             lib.longattn_status_string.argtypes = [ctypes.c_int]
             lib.longattn_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -131,6 +156,20 @@ def longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes,
 
 def longattn_count_entries(desc, entries_out, stream) -> int:
     return load().longattn_count_entries(ctypes.byref(desc), entries_out, stream)
+
+
+def longattn_decode_workspace_size(desc: longattn_decode_desc) -> Tuple[int, int]:
+    """Returns (status, bytes)."""
+    nbytes = ctypes.c_size_t(0)
+    st = load().longattn_decode_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes))
+    return st, int(nbytes.value)
+
+
+def longattn_decode(desc, q, k_cache, v_cache, out, lse, workspace, workspace_bytes,
+                    stream) -> int:
+    """Raw call; pointer arguments are integers (device addresses) or None."""
+    return load().longattn_decode(ctypes.byref(desc), q, k_cache, v_cache, out, lse, workspace,
+                                  int(workspace_bytes), stream)
 
 
 # ----------------------------------------------------------------------------- torch helpers
@@ -277,3 +316,58 @@ def from_hf_mask(mask):
     idx = torch.nonzero(is_g, as_tuple=False)[:, 1].to(torch.int32).reshape(B, g)
     key_pad = (mask == 0).to(torch.uint8)
     return idx.contiguous(), key_pad.contiguous()
+
+
+def make_decode_desc(q, k_cache, positions, *, window: int, scale: Optional[float] = None,
+                     ring: bool = False) -> longattn_decode_desc:
+    """Descriptor for q [B, H, m, d], caches [B, H, cache_len, d] and int32 positions [B]."""
+    import torch
+
+    B, H, m, d = q.shape
+    if q.dtype == torch.bfloat16:
+        dt = LONGATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = LONGATTN_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+    if positions.dtype != torch.int32 or positions.device != q.device or positions.numel() != B:
+        raise TypeError("positions must be an int32 tensor of [batch] on q's device")
+    return longattn_decode_desc(
+        batch=B, heads=H, d=d, dtype=dt,
+        scale=float(scale) if scale is not None else 1.0 / float(d) ** 0.5,
+        window=int(window), n_queries=m, cache_len=int(k_cache.shape[2]), ring=int(bool(ring)),
+        positions=positions.data_ptr(),
+    )
+
+
+def decode(q, k_cache, v_cache, positions, *, window: int, scale: Optional[float] = None,
+           ring: bool = False, out=None, lse=None, want_lse: bool = True, workspace=None,
+           stream=None):
+    """Sliding-window decode: q [B, H, m, d] rows at positions positions[b] + j attend the last
+    ``window`` keys (up to their own position) held in k_cache / v_cache [B, H, cache_len, d]
+    (slot = position, or position % cache_len when ``ring``).  Returns (out, lse)."""
+    import torch
+
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k_cache, v_cache must be contiguous device tensors")
+    if k_cache.shape != v_cache.shape or k_cache.shape[:2] != q.shape[:2] or \
+            k_cache.shape[3] != q.shape[3] or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("k_cache, v_cache must be [B, H, cache_len, d] of q's dtype")
+    positions = positions.contiguous()
+    desc = make_decode_desc(q, k_cache, positions, window=window, scale=scale, ring=ring)
+    st, ws_bytes = longattn_decode_workspace_size(desc)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_decode_workspace_size")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = longattn_decode(desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                         out.data_ptr(), _ptr(lse), _ptr(workspace) if ws_bytes else None,
+                         ws_bytes, _stream_handle(stream))
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_decode")
+    return out, lse

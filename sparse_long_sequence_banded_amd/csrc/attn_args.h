@@ -44,6 +44,35 @@ struct FwdArgs : FwdCore {
   uint8_t dil[kMaxTableHeads];
 };
 
+// Sliding-window decode over a key/value cache.
+constexpr int kDecodeGenericChunk = 256;  // cache positions per workgroup, generic head dims
+constexpr int kDecodeMaxQueries = 16;     // new rows per sample
+constexpr int kDecodeMaxDim = 256;
+
+struct DecodeArgs {
+  const void* q;            // [B][H][m][d]
+  const void* k;            // [B][H][cache_len][d]
+  const void* v;
+  void* out;                // [B][H][m][d]
+  float* lse;               // [B][H][m] or null
+  const int32_t* positions; // [B]
+  float* part;              // partial outputs [B*H*m][chunks][d], then (max, sum) [..][2]
+  int B, H, d, m;
+  int window, cache_len, ring, chunks;
+  int waves;                // waves per workgroup of the head-dim-specific kernel; 0: generic
+  float scale_log2;
+};
+
+// Work split of a decode call: `chunks` workgroups per (b, h), each covering `waves` * (its
+// positions per wave) consecutive positions (generic kernel: 256); `merge` = partials are
+// written and combined by the merge kernel (needs workspace).
+struct DecodeConfig {
+  int waves = 0;
+  long chunks = 1;
+  bool merge = true;
+};
+DecodeConfig decode_config(bool bf16, int d, long span, long bh);
+
 // Launchers (defined next to their kernels).
 int main_rows_per_workgroup(int mode, int d, int block);
 // Optional events that record a kernel's own start and end (attached to its dispatch).
@@ -56,5 +85,6 @@ hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStr
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace longattn

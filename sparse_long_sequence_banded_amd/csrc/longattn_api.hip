@@ -196,6 +196,59 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 
 }  // namespace
 
+// ------------------------------------------------------------------------------ decode
+namespace {
+
+struct DecodePlan {
+  DecodeArgs a;
+  size_t ws_bytes = 0;
+  bool empty = false;
+};
+
+longattn_status plan_decode(const longattn_decode_desc* d, DecodePlan* P) {
+  if (!d) return LONGATTN_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->heads < 0 || d->d < 1) return LONGATTN_ERR_INVALID_ARG;
+  if (d->dtype != LONGATTN_BF16 && d->dtype != LONGATTN_F32) return LONGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return LONGATTN_ERR_INVALID_ARG;
+  if (d->window < 1 || d->n_queries < 1 || d->cache_len < 1) return LONGATTN_ERR_INVALID_ARG;
+  if (d->ring != 0 && d->ring != 1) return LONGATTN_ERR_INVALID_ARG;
+  // a rolling buffer must hold every position the rows can reach
+  if (d->ring && (long)d->window + d->n_queries - 1 > d->cache_len) return LONGATTN_ERR_INVALID_ARG;
+  if (d->batch > 0 && d->heads > 0 && !d->positions) return LONGATTN_ERR_INVALID_ARG;
+  if (d->d % 8 != 0 || d->d > kDecodeMaxDim || d->n_queries > kDecodeMaxQueries)
+    return LONGATTN_ERR_UNSUPPORTED;
+  const long elem = d->dtype == LONGATTN_BF16 ? 2 : 4;
+  if ((long)d->cache_len * d->d * elem > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  const long span = (long)d->window + d->n_queries - 1;  // positions of the union of windows
+  const long bh = (long)d->batch * d->heads;
+  const DecodeConfig cfg = decode_config(d->dtype == LONGATTN_BF16, d->d, span, bh);
+  const long chunks = cfg.chunks;
+  const long rows = bh * d->n_queries;
+  if ((long)d->batch * d->heads * chunks > 0x7fffffffL || chunks > 0x7fffffffL)
+    return LONGATTN_ERR_UNSUPPORTED;
+  DecodePlan& p = *P;
+  p = DecodePlan();
+  DecodeArgs& a = p.a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = d->batch;
+  a.H = d->heads;
+  a.d = d->d;
+  a.m = d->n_queries;
+  a.window = d->window;
+  a.cache_len = d->cache_len;
+  a.ring = d->ring;
+  a.chunks = (int)chunks;
+  a.waves = cfg.waves;
+  a.scale_log2 = d->scale * 1.44269504088896340736f;
+  a.positions = d->positions;
+  p.empty = rows == 0;
+  p.ws_bytes = (p.empty || !cfg.merge) ? 0
+                                        : (size_t)rows * chunks * (size_t)(d->d + 2) * sizeof(float);
+  return LONGATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 longattn_status longattn_workspace_size(const longattn_desc* desc, size_t* bytes) {
@@ -289,6 +342,51 @@ longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entri
     a.B = a.H = a.n = 0;
   }
   const hipError_t e = launch_count_entries(a, entries_out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
+}
+
+
+longattn_status longattn_decode_workspace_size(const longattn_decode_desc* desc, size_t* bytes) {
+  if (!bytes) return LONGATTN_ERR_INVALID_ARG;
+  DecodePlan p;
+  const longattn_status st = plan_decode(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  *bytes = p.ws_bytes;
+  return LONGATTN_OK;
+}
+
+longattn_status longattn_decode(const longattn_decode_desc* desc, const void* q,
+                                const void* k_cache, const void* v_cache, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan p;
+  const longattn_status st = plan_decode(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  if (p.empty) return LONGATTN_OK;
+  if (!q || !k_cache || !v_cache || !out) return LONGATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return LONGATTN_ERR_ALIGNMENT;
+  if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes)) return LONGATTN_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return LONGATTN_ERR_HIP;
+    std::vector<int32_t> pos(desc->batch);
+    if (hipMemcpy(pos.data(), desc->positions, pos.size() * 4, hipMemcpyDeviceToHost) !=
+        hipSuccess)
+      return LONGATTN_ERR_HIP;
+    for (int32_t t0 : pos) {
+      if (t0 < 0) return LONGATTN_ERR_INVALID_ARG;
+      if (!desc->ring && (long)t0 + desc->n_queries - 1 >= desc->cache_len)
+        return LONGATTN_ERR_INVALID_ARG;
+    }
+  }
+  DecodeArgs& a = p.a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.lse = lse;
+  a.part = static_cast<float*>(workspace);
+  const hipError_t e = launch_decode(a, desc->dtype == LONGATTN_BF16, s);
   return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
 }
 

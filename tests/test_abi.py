@@ -151,3 +151,89 @@ def test_status_strings():
     for s in range(6):
         assert la.longattn_status_string(s) != "unknown status"
     assert la.longattn_status_string(42) == "unknown status"
+
+
+# ------------------------------------------------------------------------------ decode
+def test_decode_descriptor_layout_matches_the_header(tmp_path):
+    fields = [f for f, _ in la.longattn_decode_desc._fields_]
+    src = tmp_path / "dlayout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "longattn.h"\nint main(void){\n'
+        + 'printf("%zu\\n", sizeof(longattn_decode_desc));\n'
+        + "".join(f'printf("%zu\\n", offsetof(longattn_decode_desc, {f}));\n' for f in fields)
+        + "return 0;}\n")
+    exe = tmp_path / "dlayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(la.longattn_decode_desc)
+    assert vals[1:] == [getattr(la.longattn_decode_desc, f).offset for f in fields]
+
+
+def _ddesc(**kw):
+    base = dict(batch=2, heads=3, d=128, dtype=la.LONGATTN_BF16, scale=0.0884, window=512,
+                n_queries=1, cache_len=4096, ring=0, positions=FAKE)
+    base.update(kw)
+    return la.longattn_decode_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(batch=-1), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(dtype=5), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(window=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(n_queries=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(cache_len=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(ring=2), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(positions=None), la.LONGATTN_ERR_INVALID_ARG),
+    # a rolling buffer shorter than window + m - 1 would overwrite positions still needed
+    (dict(ring=1, cache_len=512, n_queries=2), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(d=100), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(d=264), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(n_queries=17), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(cache_len=1 << 23), la.LONGATTN_ERR_UNSUPPORTED),  # 2 GiB per (b, h) cache
+])
+def test_bad_decode_descriptors_are_rejected(kw, status):
+    d = _ddesc(**kw)
+    st, _ = la.longattn_decode_workspace_size(d)
+    assert st == status
+    assert la.longattn_decode(d, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == status
+
+
+def test_decode_workspace_formula_and_checks():
+    # partials: B*H*m rows x chunks x (d + 2) floats; a chunk is 4 or 8 waves of 16 loads of
+    # 16 bytes per lane (positions per wave: 64 for bf16 d=128, 64 for fp32 d=64), 4 waves when
+    # 8-wave chunks would give fewer than 512 workgroups; no workspace when one chunk covers
+    # the window
+    d = _ddesc()
+    assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 2 * 3 * 1 * 2 * 130 * 4)
+    d = _ddesc(window=4000, n_queries=5, d=64, dtype=la.LONGATTN_F32)
+    assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 2 * 3 * 5 * 16 * 66 * 4)
+    d = _ddesc(batch=32, heads=16)  # 512 workgroups of 8 waves, one per window
+    assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 0)
+    d = _ddesc(batch=32, heads=16, window=200)  # a 4-wave chunk covers the window
+    assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 0)
+    d = _ddesc(d=24, window=300, n_queries=2)  # other head dims: 256-position chunks, always
+    assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 2 * 3 * 2 * 2 * 26 * 4)
+    d = _ddesc(ring=1, cache_len=512)  # exactly window + m - 1 slots
+    st, nbytes = la.longattn_decode_workspace_size(d)
+    assert st == la.LONGATTN_OK
+    assert la.longattn_decode(d, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == \
+        la.LONGATTN_ERR_WORKSPACE
+    assert la.longattn_decode(d, FAKE, FAKE, FAKE, FAKE, None, FAKE, nbytes - 1, None) == \
+        la.LONGATTN_ERR_WORKSPACE
+    assert la.longattn_decode(d, FAKE + 8, FAKE, FAKE, FAKE, None, FAKE, nbytes, None) == \
+        la.LONGATTN_ERR_ALIGNMENT
+    assert la.longattn_decode(d, FAKE, None, FAKE, FAKE, None, FAKE, nbytes, None) == \
+        la.LONGATTN_ERR_INVALID_ARG
+
+
+def test_empty_decode_launches_nothing():
+    for kw in (dict(batch=0, positions=None), dict(heads=0, positions=None)):
+        d = _ddesc(**kw)
+        assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 0)
+        assert la.longattn_decode(d, None, None, None, None, None, None, 0, None) == \
+            la.LONGATTN_OK
