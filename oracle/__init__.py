@@ -7,7 +7,8 @@ use is the seeded input generator package ``workloads``.
 
 The arithmetic lives in ``longattn_oracle.c`` (plain C, fp64, OpenMP); what it computes and
 which passage each step follows is written at the top of that file.  ``decode_inputs`` states a
-decode step over a key/value cache as that same forward pass on the gathered window.  Every function is pinned
+decode step over a key/value cache as that same forward pass on the gathered window;
+``backward`` gives the exact gradients of the forward pass.  Every function is pinned
 by the CPU tests (dense brute force, library full/causal attention, the Big Bird worked window
 example, closed-form counts and invariants); none is left "parity unpinned".
 """
@@ -52,6 +53,11 @@ def _bind(lib):
     lib.longattn_oracle_count.restype = ctypes.c_int
     lib.longattn_oracle_count.argtypes = [
         _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _P, ctypes.c_int,
+    ]
+    lib.longattn_oracle_backward.restype = ctypes.c_int
+    lib.longattn_oracle_backward.argtypes = [
+        _I64, _I64, _I64, _I64, ctypes.c_double, _I64, _I64, _P, _P, _I64, _P, _P,
+        _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int,
     ]
     lib.longattn_oracle_row_set.restype = ctypes.c_int64
     lib.longattn_oracle_row_set.argtypes = [
@@ -138,6 +144,40 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, win_le
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out, lse, int(E.value)
+
+
+def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, *, scale: float,
+             win_left: int, win_right: int, dilation=None, global_idx=None, key_pad=None,
+             layout=None, block: int = 0, max_kb: int = 0, nthreads: int = 0
+             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients (dq, dk, dv) [B,H,n,d] fp64 of sum(dout * out) for the forward pass above."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    B, H, n, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    keep, sargs = _struct_args(B, H, n, win_left, win_right, dilation, global_idx, key_pad,
+                               layout, block, max_kb)
+    dq = np.empty_like(q)
+    dk = np.empty_like(q)
+    dv = np.empty_like(q)
+    w_l, w_r, dil, gi, g, kp, lay, blk, mkb = sargs
+    rc = _load().longattn_oracle_backward(
+        B, H, n, d, float(scale), w_l, w_r, dil, gi, g, kp, lay, blk, mkb,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return dq, dk, dv
+
+
+def backward_inputs(inp, dout: np.ndarray, nthreads: int = 0):
+    """Oracle backward on a ``workloads.Inputs`` instance and an output gradient ``dout``."""
+    return backward(inp.f64("q"), inp.f64("k"), inp.f64("v"), dout, scale=inp.scale,
+                    win_left=inp.win_left, win_right=inp.win_right, dilation=inp.dilation,
+                    global_idx=inp.global_idx, key_pad=inp.key_pad, layout=inp.layout,
+                    block=inp.block, max_kb=inp.max_kb, nthreads=nthreads)
 
 
 def count(B: int, H: int, n: int, *, win_left: int, win_right: int, dilation=None,

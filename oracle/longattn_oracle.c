@@ -33,7 +33,24 @@
  *   6. m = max s_j, w_j = exp(s_j - m), l = sum w_j, out = (sum_j w_j v[j]) / l and
  *      lse = m + log(l); sums run over S in ascending key order.
  *
- * Layout of every tensor: contiguous [batch][heads][n][d] (q, k, v, out) and
+ * Backward pass (longattn_oracle_backward).  The forward output is a differentiable function
+ * of q, k and v, and training with this attention needs its gradient (the Longformer hub page,
+ * section 3, keeps training a converted model on long documents; the SWA/Hybrid-RoPE blog,
+ * section 1, fine-tunes at 16K+ tokens).  Given the
+ * gradient dO of a loss with respect to out, the oracle writes the exact gradients dQ, dK, dV of
+ * that loss, from the chain rule through steps 5 and 6 with the same sets S:
+ *
+ *   P_j   = exp(s_j - lse)                    (the softmax weights of row i, j in S)
+ *   dP_j  = sum_c dO[i][c] * v[j][c]          (gradient of the loss w.r.t. P_j)
+ *   Drow  = sum_j P_j * dP_j                  (= sum_c dO[i][c] * out[i][c])
+ *   dS_j  = P_j * (dP_j - Drow)               (through the softmax normalisation)
+ *   dQ[i] = scale * sum_j dS_j * k[j],   dK[j] += scale * dS_j * q[i],   dV[j] += P_j * dO[i].
+ *
+ * Rows with an empty S contribute nothing (their output is the constant 0).  Each (b, h) is
+ * handled by one thread, rows in ascending order, so the sums into dK and dV run in a fixed
+ * order.
+ *
+ * Layout of every tensor: contiguous [batch][heads][n][d] (q, k, v, out, dO, dQ, dK, dV) and
  * [batch][heads][n] (lse).  All pointers are host pointers.
  */
 #include <math.h>
@@ -269,4 +286,100 @@ int64_t longattn_oracle_row_set(int64_t B, int64_t H, int64_t n, int64_t win_lef
   free(w.mark);
   free(is_global);
   return w.cnt;
+}
+
+/* Backward pass: gradients of sum(dout * out) with respect to q, k and v (see the header).
+ * dout, dq, dk, dv: [B][H][n][d] fp64; dq, dk, dv are overwritten.  Returns 0, or a negative
+ * code on bad arguments. */
+int longattn_oracle_backward(int64_t B, int64_t H, int64_t n, int64_t d, double scale,
+                             int64_t win_left, int64_t win_right, const int32_t* dilation,
+                             const int32_t* global_idx, int64_t n_global,
+                             const uint8_t* key_pad, const int32_t* layout, int64_t block,
+                             int64_t max_kb, const double* q, const double* k, const double* v,
+                             const double* dout, double* dq, double* dk, double* dv,
+                             int nthreads) {
+  problem p = {B, H, n, d, win_left, win_right, dilation, global_idx, n_global,
+               key_pad, layout, block, max_kb};
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_BAD_ARG;
+  int rc = check(&p);
+  if (rc != ORACLE_OK) return rc;
+  uint8_t* is_global = NULL;
+  if (n_global > 0 && B * n > 0) {
+    is_global = (uint8_t*)calloc((size_t)(B * n), 1);
+    if (!is_global) return ORACLE_NO_MEMORY;
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t c = 0; c < n_global; ++c) is_global[b * n + global_idx[b * n_global + c]] = 1;
+  }
+  memset(dq, 0, (size_t)(B * H * n * d) * sizeof(double));
+  memset(dk, 0, (size_t)(B * H * n * d) * sizeof(double));
+  memset(dv, 0, (size_t)(B * H * n * d) * sizeof(double));
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  int failed = 0;
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+  {
+    scratch w;
+    size_t cap = (size_t)(n > 0 ? n : 1);
+    w.mark = (int64_t*)calloc(cap, sizeof(int64_t));
+    w.keys = (int32_t*)malloc(cap * sizeof(int32_t));
+    w.s = (double*)malloc(cap * sizeof(double));
+    double* dp = (double*)malloc(cap * sizeof(double));
+    w.epoch = 0;
+    if (!w.mark || !w.keys || !w.s || !dp) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+      if (failed) continue;
+      const int64_t b = bh / H, h = bh % H;
+      const double* kb = k + bh * n * d;
+      const double* vb = v + bh * n * d;
+      double* dkb = dk + bh * n * d;
+      double* dvb = dv + bh * n * d;
+      for (int64_t i = 0; i < n; ++i) {
+        build_set(&w, &p, is_global, b, h, i);
+        if (w.cnt == 0) continue;
+        const int64_t r = bh * n + i;
+        const double* qi = q + r * d;
+        const double* doi = dout + r * d;
+        double* dqi = dq + r * d;
+        /* scores and the log-normaliser of row i, as in the forward pass */
+        double m = -INFINITY;
+        for (int64_t t = 0; t < w.cnt; ++t) {
+          const double* kj = kb + (int64_t)w.keys[t] * d;
+          double dot = 0.0;
+          for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+          w.s[t] = dot * scale;
+          if (w.s[t] > m) m = w.s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < w.cnt; ++t) l += exp(w.s[t] - m);
+        const double lse = m + log(l);
+        /* P_j, dP_j and Drow */
+        double drow = 0.0;
+        for (int64_t t = 0; t < w.cnt; ++t) {
+          const double* vj = vb + (int64_t)w.keys[t] * d;
+          double dot = 0.0;
+          for (int64_t c = 0; c < d; ++c) dot += doi[c] * vj[c];
+          w.s[t] = exp(w.s[t] - lse); /* P_j from here on */
+          dp[t] = dot;
+          drow += w.s[t] * dot;
+        }
+        /* dS_j and the three gradients */
+        for (int64_t t = 0; t < w.cnt; ++t) {
+          const int64_t j = w.keys[t];
+          const double ds = w.s[t] * (dp[t] - drow);
+          const double* kj = kb + j * d;
+          for (int64_t c = 0; c < d; ++c) {
+            dqi[c] += scale * ds * kj[c];
+            dkb[j * d + c] += scale * ds * qi[c];
+            dvb[j * d + c] += w.s[t] * doi[c];
+          }
+        }
+      }
+    }
+    free(w.mark);
+    free(w.keys);
+    free(w.s);
+    free(dp);
+  }
+  free(is_global);
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }

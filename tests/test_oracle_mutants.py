@@ -63,10 +63,38 @@ PINS = [
 ]
 
 
-def _caught(lib_path):
+# Planted mistakes in the backward pass, caught by the backward pins.
+from tests import test_oracle_backward as bpins  # noqa: E402
+
+BWD_MUTANTS = {
+    "bwd_drow_dropped": ("const double ds = w.s[t] * (dp[t] - drow);",
+                         "const double ds = w.s[t] * dp[t];"),
+    "bwd_ds_sign_flipped": ("const double ds = w.s[t] * (dp[t] - drow);",
+                            "const double ds = w.s[t] * (drow - dp[t]);"),
+    "bwd_dq_scale_dropped": ("dqi[c] += scale * ds * kj[c];", "dqi[c] += ds * kj[c];"),
+    "bwd_dk_uses_key": ("dkb[j * d + c] += scale * ds * qi[c];",
+                        "dkb[j * d + c] += scale * ds * kj[c];"),
+    "bwd_dv_uses_ds": ("dvb[j * d + c] += w.s[t] * doi[c];", "dvb[j * d + c] += ds * doi[c];"),
+    "bwd_dp_against_keys": ("const double* vj = vb + (int64_t)w.keys[t] * d;\n          double dot = 0.0;\n          for (int64_t c = 0; c < d; ++c) dot += doi[c] * vj[c];",
+                            "const double* vj = kb + (int64_t)w.keys[t] * d;\n          double dot = 0.0;\n          for (int64_t c = 0; c < d; ++c) dot += doi[c] * vj[c];"),
+    "bwd_unnormalised_weights": ("w.s[t] = exp(w.s[t] - lse); /* P_j from here on */",
+                                 "w.s[t] = exp(w.s[t] - m); /* P_j from here on */"),
+    "bwd_dq_of_other_head": ("double* dqi = dq + r * d;", "double* dqi = dq + (r % n) * d;"),
+}
+
+BWD_PINS = [
+    lambda: [bpins.test_backward_matches_finite_differences_of_the_forward(c) for c in bpins.SMALL],
+    lambda: [bpins.test_backward_matches_autograd_of_dense_masked_attention(c)
+             for c in bpins.BRUTE],
+    bpins.test_key_gradients_sum_to_zero_and_value_gradients_to_the_output_gradients,
+    bpins.test_window_zero_passes_the_gradient_to_v_only,
+]
+
+
+def _caught(lib_path, pins_list=None):
     failures = 0
     with oracle.substituted_library(lib_path):
-        for pin in PINS:
+        for pin in (PINS if pins_list is None else pins_list):
             try:
                 pin()
             except (AssertionError, ValueError):
@@ -87,8 +115,22 @@ def test_planted_mistake_is_caught(name, tmp_path):
     assert _caught(str(so)) >= 1, f"no pin catches the planted mistake {name}"
 
 
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_planted_backward_mistake_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(mutant_c), "-lm"], check=True, capture_output=True)
+    assert _caught(str(so), BWD_PINS) >= 1, f"no pin catches the planted mistake {name}"
+
+
 def test_unmutated_copy_passes_every_pin(tmp_path):
     so = tmp_path / "libcopy.so"
     subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
                     SRC, "-lm"], check=True, capture_output=True)
     assert _caught(str(so)) == 0
+    assert _caught(str(so), BWD_PINS) == 0
