@@ -114,6 +114,32 @@ longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entri
                                        void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Backward pass.
+ *
+ * Gradients of a loss through the forward pass above, for training with this attention (the
+ * Longformer hub page, section 3: a converted model keeps training on long documents; the
+ * SWA/Hybrid-RoPE blog, section 1: a 16K+ fine-tuning stage).  Given dout = dLoss/dout, it writes
+ * dq, dk, dv = dLoss/dq, dLoss/dk, dLoss/dv of the same descriptor's attention:
+ *   P_ij = exp(scale * q_i . k_j - lse_i) for j in S(b, h, i),  Drow_i = dout_i . out_i,
+ *   dS_ij = P_ij * (dout_i . v_j - Drow_i),
+ *   dq_i = scale * sum_j dS_ij k_j,  dk_j = scale * sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i.
+ * Rows with an empty key set (lse = -inf) contribute nothing.  out and lse must be the forward
+ * pass's outputs for the same q, k, v and descriptor (the saved log-normaliser replaces the
+ * softmax recomputation).
+ *
+ * q, k, v, out, dout: DEVICE [B][H][n][d] inputs (desc->dtype); lse: DEVICE fp32 [B][H][n];
+ * dq, dk, dv: DEVICE [B][H][n][d] outputs (desc->dtype), overwritten, not aliasing any input.
+ * Every (b, h) position gets a value (0 where no edge touches it).  workspace: DEVICE scratch of
+ * at least longattn_backward_workspace_size bytes.  Kernels: every pattern for d <= 256 in both
+ * dtypes (fp32 arithmetic); status rules as longattn_forward.
+ * --------------------------------------------------------------------------------------- */
+longattn_status longattn_backward_workspace_size(const longattn_desc* desc, size_t* bytes);
+longattn_status longattn_backward(const longattn_desc* desc, const void* q, const void* k,
+                                  const void* v, const void* out, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Sliding-window decode over a key/value cache.
  *
  * The incremental form of the causal sliding window used by the SWA decoder layers (SWAN-GPT

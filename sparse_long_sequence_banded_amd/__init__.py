@@ -6,9 +6,10 @@ library's HIP kernels.  PyTorch supplies device memory and the current HIP strea
 library has not been built, every call raises ``LongAttnNotBuilt``; there is no fallback.
 
 The C entry points keep their names here (``longattn_forward``, ``longattn_workspace_size``,
-``longattn_forward_marked``, ``longattn_count_entries``, ``longattn_decode``,
-``longattn_decode_workspace_size``, ``longattn_status_string``); the ``forward`` /
-``count_entries`` / ``decode`` helpers wrap them for torch tensors.
+``longattn_forward_marked``, ``longattn_count_entries``, ``longattn_backward``,
+``longattn_backward_workspace_size``, ``longattn_decode``, ``longattn_decode_workspace_size``,
+``longattn_status_string``); the ``forward`` / ``backward`` / ``count_entries`` / ``decode``
+helpers wrap them for torch tensors.
 """
 
 import ctypes
@@ -34,6 +35,8 @@ EXPORTED = (
     "longattn_forward",
     "longattn_forward_marked",
     "longattn_count_entries",
+    "longattn_backward_workspace_size",
+    "longattn_backward",
     "longattn_decode_workspace_size",
     "longattn_decode",
     "longattn_status_string",
@@ -114,6 +117,10 @@ def load():
             lib.longattn_forward_marked.restype = ctypes.c_int
             lib.longattn_count_entries.argtypes = [D, P, P]
             lib.longattn_count_entries.restype = ctypes.c_int
+            lib.longattn_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+            lib.longattn_backward_workspace_size.restype = ctypes.c_int
+            lib.longattn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.longattn_backward.restype = ctypes.c_int
             DD = ctypes.POINTER(longattn_decode_desc)
             lib.longattn_decode_workspace_size.argtypes = [DD, ctypes.POINTER(ctypes.c_size_t)]
             lib.longattn_decode_workspace_size.restype = ctypes.c_int
@@ -156,6 +163,20 @@ def longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes,
 
 def longattn_count_entries(desc, entries_out, stream) -> int:
     return load().longattn_count_entries(ctypes.byref(desc), entries_out, stream)
+
+
+def longattn_backward_workspace_size(desc: longattn_desc) -> Tuple[int, int]:
+    """Returns (status, bytes)."""
+    nbytes = ctypes.c_size_t(0)
+    st = load().longattn_backward_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes))
+    return st, int(nbytes.value)
+
+
+def longattn_backward(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                      stream) -> int:
+    """Raw call; pointer arguments are integers (device addresses) or None."""
+    return load().longattn_backward(ctypes.byref(desc), q, k, v, out, lse, dout, dq, dk, dv,
+                                    workspace, int(workspace_bytes), stream)
 
 
 def longattn_decode_workspace_size(desc: longattn_decode_desc) -> Tuple[int, int]:
@@ -277,6 +298,43 @@ def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_forward")
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, *, scale: Optional[float] = None, win_left: int = -1,
+             win_right: int = -1, dilation=None, global_idx=None, key_pad=None,
+             block_layout=None, block: int = 0, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients (dq, dk, dv) of a loss through ``forward``, given out and lse of that forward
+    pass and dout = dLoss/dout (torch device tensors [B, H, n, d], lse [B, H, n] fp32)."""
+    import torch
+
+    for t in (q, k, v, out, dout, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v, out, lse, dout must be contiguous device tensors")
+    for t in (k, v, out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("k, v, out, dout must share q's shape and dtype")
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:3]:
+        raise ValueError("lse must be float32 [B, H, n]")
+    desc, keep = make_desc(q, scale=scale, win_left=win_left, win_right=win_right,
+                           dilation=dilation, global_idx=global_idx, key_pad=key_pad,
+                           block_layout=block_layout, block=block)
+    st, ws_bytes = longattn_backward_workspace_size(desc)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_backward_workspace_size")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = longattn_backward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                           _stream_handle(stream))
+    del keep
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_backward")
+    return dq, dk, dv
 
 
 def count_entries(q, *, win_left: int = -1, win_right: int = -1, dilation=None,

@@ -44,6 +44,16 @@ struct FwdArgs : FwdCore {
   uint8_t dil[kMaxTableHeads];
 };
 
+// Backward-pass pointers (the forward's q, k, v, lse, pattern and scale come in FwdArgs).
+struct BwdArgs {
+  const void* out;   // [B][H][n][d] forward output
+  const void* dout;  // [B][H][n][d] gradient of the loss w.r.t. out
+  void* dq;          // [B][H][n][d] outputs
+  void* dk;
+  void* dv;
+  float* drow;       // [B][H][n] workspace: dO . O per row
+};
+
 // Sliding-window decode over a key/value cache.
 constexpr int kDecodeGenericChunk = 256;  // cache positions per workgroup, generic head dims
 constexpr int kDecodeMaxQueries = 16;     // new rows per sample
@@ -86,5 +96,8 @@ hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s, const L
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_rowdot(const BwdArgs& g, long rows, int d, bool bf16, hipStream_t s);
+hipError_t launch_bwd_rowwise(const FwdArgs& a, const BwdArgs& g, int d, bool bf16,
+                              hipStream_t s);
 
 }  // namespace longattn

@@ -196,6 +196,22 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 
 }  // namespace
 
+// ------------------------------------------------------------------------------ backward
+namespace {
+
+// The backward pass: Drow per row, then dQ per query row and dK, dV per key column.
+longattn_status plan_backward(const longattn_desc* d, Plan* P) {
+  const longattn_status st = plan_call(d, false, P);
+  if (st != LONGATTN_OK) return st;
+  if (d->d > 256) return LONGATTN_ERR_UNSUPPORTED;
+  Plan& p = *P;
+  if ((long)p.a.B * p.a.H * p.a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  p.ws_bytes = p.empty ? 0 : (size_t)p.a.B * p.a.H * p.a.n * sizeof(float);
+  return LONGATTN_OK;
+}
+
+}  // namespace
+
 // ------------------------------------------------------------------------------ decode
 namespace {
 
@@ -345,6 +361,56 @@ longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entri
   return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
 }
 
+
+longattn_status longattn_backward_workspace_size(const longattn_desc* desc, size_t* bytes) {
+  if (!bytes) return LONGATTN_ERR_INVALID_ARG;
+  Plan p;
+  const longattn_status st = plan_backward(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  *bytes = p.ws_bytes;
+  return LONGATTN_OK;
+}
+
+longattn_status longattn_backward(const longattn_desc* desc, const void* q, const void* k,
+                                  const void* v, const void* out, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  longattn_status st = plan_backward(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  if (p.empty) return LONGATTN_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+    return LONGATTN_ERR_INVALID_ARG;
+  for (const void* x : {q, k, v, out, dout, static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv)})
+    if (!aligned16(x)) return LONGATTN_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return LONGATTN_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    st = debug_check(desc, s);
+    if (st != LONGATTN_OK) return st;
+  }
+  FwdArgs& a = p.a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.lse = const_cast<float*>(lse);  // read only by the backward kernels
+  a.gidx = desc->n_global > 0 ? desc->global_idx : nullptr;
+  a.kpad = desc->key_pad;
+  a.layout = desc->block_layout;
+  BwdArgs g;
+  g.out = out;
+  g.dout = dout;
+  g.dq = dq;
+  g.dk = dk;
+  g.dv = dv;
+  g.drow = static_cast<float*>(workspace);
+  const long rows = (long)a.B * a.H * a.n;
+  hipError_t e = launch_bwd_rowdot(g, rows, desc->d, p.bf16, s);
+  if (e == hipSuccess) e = launch_bwd_rowwise(a, g, desc->d, p.bf16, s);
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
+}
 
 longattn_status longattn_decode_workspace_size(const longattn_decode_desc* desc, size_t* bytes) {
   if (!bytes) return LONGATTN_ERR_INVALID_ARG;

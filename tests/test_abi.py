@@ -237,3 +237,37 @@ def test_empty_decode_launches_nothing():
         assert la.longattn_decode_workspace_size(d) == (la.LONGATTN_OK, 0)
         assert la.longattn_decode(d, None, None, None, None, None, None, 0, None) == \
             la.LONGATTN_OK
+
+
+# ------------------------------------------------------------------------------ backward
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(win_left=-1, win_right=4), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(n_global=3), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(d=300), la.LONGATTN_ERR_UNSUPPORTED),
+])
+def test_bad_backward_descriptors_are_rejected(kw, status):
+    d = _desc(**kw)
+    assert la.longattn_backward_workspace_size(d)[0] == status
+    assert la.longattn_backward(d, *([FAKE] * 9), FAKE, 1 << 30, None) == status
+
+
+def test_backward_workspace_and_pointer_checks():
+    d = _desc(batch=2, heads=3, n=500, d=40, dtype=la.LONGATTN_F32)
+    st, nbytes = la.longattn_backward_workspace_size(d)
+    assert st == la.LONGATTN_OK and nbytes == 2 * 3 * 500 * 4  # one float per row
+    # layouts combined with a window are fine for the backward in both dtypes
+    dl = _desc(block_layout=FAKE, block=16, max_kb=2)
+    assert la.longattn_backward_workspace_size(dl)[0] == la.LONGATTN_OK
+    args = [FAKE] * 9
+    assert la.longattn_backward(d, *args, None, 0, None) == la.LONGATTN_ERR_WORKSPACE
+    assert la.longattn_backward(d, *args, FAKE, nbytes - 1, None) == la.LONGATTN_ERR_WORKSPACE
+    for slot in range(9):
+        bad = list(args)
+        bad[slot] = None
+        assert la.longattn_backward(d, *bad, FAKE, nbytes, None) == la.LONGATTN_ERR_INVALID_ARG
+        bad[slot] = FAKE + (2 if slot == 4 else 8)  # lse needs 4-byte alignment, tensors 16
+        assert la.longattn_backward(d, *bad, FAKE, nbytes, None) == la.LONGATTN_ERR_ALIGNMENT
+    assert la.longattn_backward_workspace_size(_desc(n=0)) == (la.LONGATTN_OK, 0)
+    assert la.longattn_backward(_desc(n=0), *([None] * 9), None, 0, None) == la.LONGATTN_OK

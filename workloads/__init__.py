@@ -12,9 +12,11 @@ from .gen import (
     Inputs,
     bf16_bits_to_f32,
     bigbird_layout,
+    draw_dout,
     make_inputs,
     random_case,
     round_to_bf16_bits,
+    widen,
 )
 
 __all__ = [
@@ -24,7 +26,9 @@ __all__ = [
     "Inputs",
     "bf16_bits_to_f32",
     "bigbird_layout",
+    "draw_dout",
     "make_inputs",
     "random_case",
     "round_to_bf16_bits",
+    "widen",
 ]

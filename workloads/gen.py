@@ -253,3 +253,20 @@ def random_case(seed: int, *, batch: int, heads: int, n: int, d: int, dtype: str
         win_left=win_left, win_right=win_right, dilation=dil, global_idx=gidx,
         key_pad=kp, layout=lay, block=block, max_kb=max_kb,
     )
+
+
+def draw_dout(inp: Inputs, seed: int, scale: float = 1.0) -> np.ndarray:
+    """A seeded output gradient dO of q's shape: N(0, 1) * scale draws, rounded once to bf16 for
+    bf16 inputs (uint16 bit patterns), float32 otherwise."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(inp.q.shape, dtype=np.float32)
+    if scale != 1.0:
+        g *= np.float32(scale)
+    return round_to_bf16_bits(g) if inp.dtype == "bf16" else g
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 copy of a bf16 (uint16 bits) or float32 array."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
