@@ -130,14 +130,28 @@ longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entri
  * q, k, v, out, dout: DEVICE [B][H][n][d] inputs (desc->dtype); lse: DEVICE fp32 [B][H][n];
  * dq, dk, dv: DEVICE [B][H][n][d] outputs (desc->dtype), overwritten, not aliasing any input.
  * Every (b, h) position gets a value (0 where no edge touches it).  workspace: DEVICE scratch of
- * at least longattn_backward_workspace_size bytes.  Kernels: every pattern for d <= 256 in both
- * dtypes (fp32 arithmetic); status rules as longattn_forward.
+ * at least longattn_backward_workspace_size bytes.  Kernels: bf16 with d in {64, 128} and no
+ * block layout runs on matrix cores (bf16 operands, fp32 accumulation; within the forward's
+ * bf16 limits); every other pattern with d <= 256, in both dtypes, on per-row kernels with fp32
+ * arithmetic.  Status rules as longattn_forward.
  * --------------------------------------------------------------------------------------- */
 longattn_status longattn_backward_workspace_size(const longattn_desc* desc, size_t* bytes);
 longattn_status longattn_backward(const longattn_desc* desc, const void* q, const void* k,
                                   const void* v, const void* out, const float* lse,
                                   const void* dout, void* dq, void* dk, void* dv,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same pass with caller-created hipEvent_t handles that time its phases: marks[0..1] the
+ * start and end of the row preparation (Drow, lse in log2 units), marks[2..3] of the dQ kernel,
+ * marks[4..5] of the dK/dV kernel (matrix-core path: attached to the kernels' dispatches; the
+ * global-row combines fall outside them).  On the per-row path marks[0..1] bracket Drow and
+ * marks[2..5] the dQ and dK/dV kernels together.  n_marks: 0 or LONGATTN_BWD_N_MARKS. */
+#define LONGATTN_BWD_N_MARKS 6
+longattn_status longattn_backward_marked(const longattn_desc* desc, const void* q,
+                                         const void* k, const void* v, const void* out,
+                                         const float* lse, const void* dout, void* dq, void* dk,
+                                         void* dv, void* workspace, size_t workspace_bytes,
+                                         void* stream, void* const* marks, int32_t n_marks);
 
 /* ---------------------------------------------------------------------------------------
  * Sliding-window decode over a key/value cache.

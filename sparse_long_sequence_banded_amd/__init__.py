@@ -29,6 +29,7 @@ LONGATTN_ERR_HIP = 5
 LONGATTN_BF16 = 0
 LONGATTN_F32 = 1
 LONGATTN_N_MARKS = 4
+LONGATTN_BWD_N_MARKS = 6
 
 EXPORTED = (
     "longattn_workspace_size",
@@ -37,6 +38,7 @@ EXPORTED = (
     "longattn_count_entries",
     "longattn_backward_workspace_size",
     "longattn_backward",
+    "longattn_backward_marked",
     "longattn_decode_workspace_size",
     "longattn_decode",
     "longattn_status_string",
@@ -121,6 +123,11 @@ def load():
             lib.longattn_backward_workspace_size.restype = ctypes.c_int
             lib.longattn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
             lib.longattn_backward.restype = ctypes.c_int
+            lib.longattn_backward_marked.argtypes = [D, P, P, P, P, P, P, P, P, P, P,
+                                                     ctypes.c_size_t, P,
+                                                     ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_int32]
+            lib.longattn_backward_marked.restype = ctypes.c_int
             DD = ctypes.POINTER(longattn_decode_desc)
             lib.longattn_decode_workspace_size.argtypes = [DD, ctypes.POINTER(ctypes.c_size_t)]
             lib.longattn_decode_workspace_size.restype = ctypes.c_int
@@ -177,6 +184,15 @@ def longattn_backward(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace, work
     """Raw call; pointer arguments are integers (device addresses) or None."""
     return load().longattn_backward(ctypes.byref(desc), q, k, v, out, lse, dout, dq, dk, dv,
                                     workspace, int(workspace_bytes), stream)
+
+
+def longattn_backward_marked(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace,
+                             workspace_bytes, stream, marks) -> int:
+    """Raw call with LONGATTN_BWD_N_MARKS event handles (integers) in ``marks``."""
+    arr = (ctypes.c_void_p * len(marks))(*marks)
+    return load().longattn_backward_marked(ctypes.byref(desc), q, k, v, out, lse, dout, dq, dk,
+                                           dv, workspace, int(workspace_bytes), stream, arr,
+                                           len(marks))
 
 
 def longattn_decode_workspace_size(desc: longattn_decode_desc) -> Tuple[int, int]:

@@ -52,7 +52,9 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* drow;       // [B][H][n] workspace: dO . O per row
+  float* lse2;       // [B][H][n] workspace: lse in log2 units (matrix-core path)
 };
+enum BwdKind : int { kBwdDQ = 0, kBwdDKV = 1 };
 
 // Sliding-window decode over a key/value cache.
 constexpr int kDecodeGenericChunk = 256;  // cache positions per workgroup, generic head dims
@@ -99,5 +101,8 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& g, long rows, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_rowwise(const FwdArgs& a, const BwdArgs& g, int d, bool bf16,
                               hipStream_t s);
+// ev: null or three start/stop pairs (prep, dQ kernel, dK/dV kernel)
+hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, long grid, hipStream_t s,
+                           const LaunchEvents* ev);
 
 }  // namespace longattn

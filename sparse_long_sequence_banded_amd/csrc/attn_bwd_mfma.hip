@@ -1,0 +1,705 @@
+// bf16 backward pass of the window / dilation / global-token pattern on gfx950 matrix cores.
+//
+// With the forward's log-normaliser of every query row (kept in log2 units, lse2), the softmax
+// weights of an edge are recomputed directly, P = 2^(c2 s - lse2), c2 = scale * log2(e), so no
+// online softmax is needed.  For an edge (query i, key j), with Drow_i = dO_i . O_i:
+//   dP = dO_i . v_j,  dS = P (dP - Drow_i),
+//   dQ_i += scale * dS k_j,  dK_j += scale * dS q_i,  dV_j += P dO_i.
+// Every gradient row has one owner, so there are no atomics.  Two launches of one kernel
+// template:
+//   dQ kind:   a wave owns 32 query rows (its Q and dO rows are MFMA B operands held in
+//              registers) and streams 64-key tiles of K and V through LDS, like the forward pass;
+//   dK/dV kind: a wave owns 32 key rows (K and V rows in registers) and streams 64-row tiles of
+//              Q and dO through LDS, with each streamed row's lse2 and Drow.
+// In both, the streamed rows s of owner row o satisfy o - WL <= s <= o + WR in the residue
+// subsequence of the dilation (the window splits into independent undilated windows on the
+// residue classes; Longformer hub page, section 2): (WL, WR) = (win_left, win_right) for the dQ
+// kind and (win_right, win_left) for the dK/dV kind, because key j is in the window of query i
+// exactly when i is in the mirrored window of j.
+//
+// Global tokens (Longformer hub page, section 2; Big Bird reading notes, section 3.2.3): window
+// tiles drop the streamed rows that are global tokens (their edges go through the global paths,
+// each edge counted once, as in the forward pass); window workgroups then walk the global rows
+// as gathered tiles (global keys for dQ, global query rows for dK/dV).  The owners that are global
+// tokens (global query rows for dQ, global keys for dK/dV) get their own workgroups, one per
+// (batch, head, 128 global rows, 1024-row chunk), which stream every position of the chunk and
+// write fp32 partial sums; a combine kernel adds the chunks and overwrites those rows.
+//
+// Wave-level math (32x32x16 bf16 MFMA, fp32 accumulate).  Scores come out as C[streamed row]
+// [owner row]: every lane holds one owner row (its column) against 32 streamed rows.  The
+// gradient sums are kept transposed, G^T[d][owner] += X^T[d][streamed] C[streamed][owner], so
+// the C blocks (P or dS, rounded to bf16) serve directly as B operands and X^T is read from LDS
+// with the transposing 64-bit read.  Streamed matrices read both ways use the transposing
+// layout's swizzle.
+
+#include <type_traits>
+
+#include <hip/hip_ext.h>
+
+#include "attn_args.h"
+#include "mfma_util.h"
+
+namespace longattn {
+namespace {
+
+using namespace mfma;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kBwdPadWords = 64;  // staged key-padding and global-row bits: 4096 positions
+
+template <int D>
+struct BwdSmem {
+  __attribute__((aligned(1024))) unsigned char stage_a[2][kKeyTile * D * 2];  // K or Q
+  __attribute__((aligned(1024))) unsigned char stage_b[2][kKeyTile * D * 2];  // V or dO
+  __attribute__((aligned(16))) float row_l[2][kKeyTile];  // dK/dV: lse2 of the streamed rows
+  __attribute__((aligned(16))) float row_d[2][kKeyTile];  // dK/dV: Drow of the streamed rows
+  __attribute__((aligned(16))) int g_pos[kGlobalCap];     // global rows: positions
+  unsigned long long g_valid[kGlobalCap / 64];             // global rows: usable bits
+  unsigned long long g_bits[kBwdPadWords];                 // global rows among window rows
+  unsigned long long pad_bits[kBwdPadWords];               // dQ: key padding of window keys
+};
+
+struct STile {
+  int gathered;  // 0: row r at position base + kst * r; 1: row r is global row base + r
+  int base;
+  int count;     // rows >= count do not exist
+  int ks0;       // window tiles: residue-subsequence index of row 0
+};
+
+template <int D, int KIND>
+__global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
+  __shared__ BwdSmem<D> sm;
+  const FwdCore a = args;
+  const BwdArgs gp = gargs;
+  const int total = gridDim.x;
+  const int Lid = xcd_remap(blockIdx.x, total);
+  const int n_glob_wg = a.grid_rows;
+  // global-owner workgroups first (they walk 1024-row chunks), then the window workgroups
+  const int gi = Lid < n_glob_wg ? Lid : -1;
+  const int mi = Lid - n_glob_wg;
+
+  int main_b = 0, main_h = 0, main_dl = 1, main_r = 0;
+  if (gi < 0) {
+    main_b = mi / a.tiles_per_b;
+    int r = mi - main_b * a.tiles_per_b;
+    if (a.uniform_dil > 0) {
+      const int tph = args.tile_off[1];
+      main_h = r / tph;
+      r -= main_h * tph;
+      main_dl = a.uniform_dil;
+    } else {
+      int lo = 0, hi = a.H - 1;  // last head with tile_off[h] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (args.tile_off[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      main_h = lo;
+      r -= args.tile_off[main_h];
+      main_dl = args.dil[main_h];
+    }
+    main_r = r;
+  }
+
+  auto body = [&](auto mode_c, const int wg) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool DQ = KIND == kBwdDQ;
+    constexpr int NW = 4, NT = 256, RW = 32, QT = NW * RW;
+    constexpr int CH = D / 8;          // 16-byte chunks per row
+    constexpr int KS = D / 16;         // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;         // 32-row blocks of a transposed gradient
+    constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (matrix A, then B)
+    constexpr int LPW = NLOAD / NW;
+    constexpr int RPB = 64 / CH;       // rows per 1 KB block
+    constexpr bool kGathered = MODE == kBand;  // window workgroups also walk the global rows
+    static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
+    static_assert(kGlobalCap == NT, "one global row per thread when staging");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qj = lane & 31, hh = lane >> 5;
+    const int WL = DQ ? a.wl : a.wr, WR = DQ ? a.wr : a.wl;
+
+    // ------------------------------------------------------------------ work decomposition
+    int b = 0, h = 0, dl = 1, p = 0, np = a.n, o0 = 0, ck = 0, rg = 0;
+    if constexpr (MODE == kGlobalRows) {
+      const int rgs = (a.g + QT - 1) / QT;
+      int x = wg;
+      ck = x % a.chunks;
+      x /= a.chunks;
+      rg = x % rgs;
+      x /= rgs;
+      h = x % a.H;
+      b = x / a.H;
+    } else {
+      (void)wg;
+      b = main_b;
+      h = main_h;
+      dl = main_dl;
+      int r = main_r;
+      for (;;) {  // residue class p holds ceil((n - p) / dl) positions
+        const int n_p = (a.n - p + dl - 1) / dl;
+        const int t_p = (n_p + QT - 1) / QT;
+        if (r < t_p) { np = n_p; break; }
+        r -= t_p;
+        ++p;
+      }
+      o0 = r * QT;
+    }
+    const int kst = (MODE == kBand) ? min(dl, a.n) : 1;
+    const long bh = (long)b * a.H + h;
+    const uint16_t* dOb = static_cast<const uint16_t*>(gp.dout) + bh * a.n * D;
+    const uint16_t* SA = (DQ ? a.k : a.q) + bh * a.n * D;   // streamed matrix A
+    const uint16_t* SB = DQ ? a.v + bh * a.n * D : dOb;     // streamed matrix B
+    const uint16_t* OA = (DQ ? a.q : a.k) + bh * a.n * D;   // owner matrix A
+    const uint16_t* OB = DQ ? dOb : a.v + bh * a.n * D;     // owner matrix B
+    const float* l2b = gp.lse2 + bh * a.n;
+    const float* drb = gp.drow + bh * a.n;
+    const uint8_t* pad = a.kpad ? a.kpad + (long)b * a.n : nullptr;
+    const int* gb = a.gidx ? a.gidx + (long)b * a.g : nullptr;
+
+    // ------------------------------------------------------------------ owner row of this lane
+    int opos = -1, osub = 0;
+    {
+      const int orow = wave * RW + qj;
+      if constexpr (MODE == kBand) {
+        osub = o0 + orow;
+        if (osub < np) opos = p + dl * osub;
+      } else {
+        const int c = rg * QT + orow;
+        if (c < a.g) {
+          const int x = gb[c];
+          if (x >= 0 && x < a.n) opos = x;
+        }
+      }
+    }
+    // ------------------------------------------------------------------ streamed tiles
+    int n_local = 0, s_lo = 0, s_hi = -1;
+    if constexpr (MODE == kBand) {
+      if (a.band_on) {
+        const int o_last = min(o0 + QT, np) - 1;
+        s_lo = max(0, o0 - WL);
+        s_hi = min(np - 1, o_last + WR);
+        n_local = (s_hi >= s_lo) ? (s_hi - s_lo + kKeyTile) / kKeyTile : 0;
+      }
+    } else {
+      const int c0 = ck * kGlobalChunk;
+      const int c1 = min(a.n, c0 + kGlobalChunk);
+      n_local = (c1 > c0) ? (c1 - c0 + kKeyTile - 1) / kKeyTile : 0;
+      s_lo = c0;
+      s_hi = c1 - 1;
+    }
+    const int n_gtiles = (kGathered && a.g > 0) ? (a.g + kKeyTile - 1) / kKeyTile : 0;
+    const int n_tiles = n_local + n_gtiles;
+
+    auto tile_of = [&](int t) -> STile {
+      STile T;
+      T.ks0 = 0;
+      if (t >= n_local) {
+        T.gathered = 1;
+        T.base = (t - n_local) * kKeyTile;
+        T.count = min(kKeyTile, a.g - T.base);
+      } else if constexpr (MODE == kBand) {
+        T.gathered = 0;
+        T.ks0 = s_lo + t * kKeyTile;
+        T.base = p + dl * T.ks0;
+        T.count = min(kKeyTile, np - T.ks0);
+      } else {
+        T.gathered = 0;
+        T.base = s_lo + t * kKeyTile;
+        T.count = min(kKeyTile, s_hi + 1 - T.base);
+      }
+      return T;
+    };
+
+    // ------------------------------------------------------------------ tile loading
+    // Waves 0-1 move matrix A's 1 KB blocks, waves 2-3 matrix B's (block `sub` holds rows
+    // RPB*sub .. +RPB-1; lane l moves row RPB*sub + l/CH, chunk l%CH, to its swizzled slot).
+    // For dK/dV, wave 0 also moves the tile rows' lse2 and wave 1 their Drow (4 bytes a lane).
+    const int mat = (wave * LPW) / CH;
+    const int sub0 = (wave * LPW) % CH;
+    const bool vlayout = (mat == 0) || !DQ;  // matrices read transposed use that layout
+    auto ld_row = [&](int j) -> int { return (sub0 + j) * RPB + lane / CH; };
+    auto ld_col = [&](int j) -> int {
+      const int row = ld_row(j);
+      return 8 * ((lane % CH) ^ (vlayout ? swz_v<D>(row) : swz_k<D>(row)));
+    };
+    uint32_t voff[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      voff[j] = (uint32_t)(min((long)ld_row(j) * kst, (long)a.n) * D + ld_col(j)) * 2u;
+    const uint16_t* msrc = (mat == 0) ? SA : SB;
+    const bool row_wave = !DQ && wave < 2;
+    const float* row_src = wave == 0 ? l2b : drb;
+    auto issue = [&](int si, const STile& T) {
+      unsigned char* stg = mat == 0 ? sm.stage_a[si] : sm.stage_b[si];
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stg + sub0 * 1024));
+      if (kGathered && T.gathered) {
+        const u32x4 rs = buf_rsrc(msrc, (uint32_t)a.n * D * 2u);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const int pos = sm.g_pos[T.base + min(ld_row(j), T.count - 1)];
+          lds_dma16(rs, (uint32_t)(pos * D + ld_col(j)) * 2u, dst + 1024 * j);
+        }
+      } else {
+        const u32x4 rs = buf_rsrc(msrc + (long)T.base * D, (uint32_t)(a.n - T.base) * D * 2u);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) lds_dma16(rs, voff[j], dst + 1024 * j);
+      }
+      if (row_wave) {
+        float* rdst = wave == 0 ? sm.row_l[si] : sm.row_d[si];
+        const uint32_t dw = __builtin_amdgcn_readfirstlane(lds_addr(rdst));
+        uint32_t off;
+        if (kGathered && T.gathered)
+          off = (uint32_t)sm.g_pos[T.base + min(lane, T.count - 1)] * 4u;
+        else
+          off = lane < T.count ? (uint32_t)(T.base + kst * lane) * 4u : (uint32_t)a.n * 4u;
+        lds_dma4(buf_rsrc(row_src, (uint32_t)a.n * 4u), off, dw);
+      }
+    };
+
+    // Global rows first (positions feed the gathered tiles and the window-tile exclusion), then
+    // the first window tile, the owner fragments and the staging.
+    int gx = a.n;
+    if (kGathered && n_gtiles > 0 && tid < a.g) gx = gb[tid];
+    if (n_local > 0) issue(0, tile_of(0));
+
+    // Owner fragments (B operands): lane (qj, hh) holds d = 16ks + 8hh .. +7 of its owner row.
+    const float c2 = a.scale_log2;
+    u32x4 fa[KS], fb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      fa[s] = u32x4{0, 0, 0, 0};
+      fb[s] = u32x4{0, 0, 0, 0};
+      if (opos >= 0) {
+        fa[s] = *reinterpret_cast<const u32x4*>(OA + (long)opos * D + 16 * s + 8 * hh);
+        fb[s] = *reinterpret_cast<const u32x4*>(OB + (long)opos * D + 16 * s + 8 * hh);
+      }
+    }
+    float o_l2 = 0.f, o_dr = 0.f;  // dQ: the owner query's lse2 and Drow
+    bool own_ok = opos >= 0;       // dK/dV: the owner key exists and is not padded
+    if constexpr (DQ) {
+      if (opos >= 0) {
+        o_l2 = l2b[opos];
+        o_dr = drb[opos];
+      }
+    } else {
+      if (own_ok && pad) own_ok = pad[opos] == 0;
+    }
+
+    // ------------------------------------------------------------------ staging in LDS
+    // Usable global rows: dQ streams global keys (in range, not padded); dK/dV streams global
+    // query rows (in range).  Window tiles drop them (g_bits over the window range when it fits,
+    // else a search of the sorted positions).
+    const bool gbits_staged = kGathered && n_gtiles > 0 && n_local <= kBwdPadWords;
+    if constexpr (kGathered) {
+      if (n_gtiles > 0) {
+        if (gbits_staged) {
+          for (int w = tid; w < n_local; w += NT) sm.g_bits[w] = 0ull;
+          __syncthreads();
+        }
+        const int x = gx;
+        bool ok = tid < a.g && x >= 0 && x < a.n;
+        if constexpr (DQ) {
+          if (ok && pad) ok = pad[x] == 0;
+        }
+        const int pos = min(max(x, 0), a.n);
+        const int rel = pos - p;
+        if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
+          const int j = rel / dl - s_lo;
+          if (j >= 0 && j < kKeyTile * n_local) atomicOr(&sm.g_bits[j >> 6], 1ull << (j & 63));
+        }
+        sm.g_pos[tid] = pos;
+        const unsigned long long vm = __ballot(ok);
+        if (lane == 0) sm.g_valid[tid >> 6] = vm;
+      }
+    }
+    // dQ: key padding of the reachable window positions as bits, when they fit.
+    int pad_lo = 0;
+    bool pad_staged = false;
+    if (DQ && pad && n_local > 0) {
+      long lo, hi;
+      if constexpr (MODE == kBand) {
+        lo = p + (long)dl * s_lo;
+        hi = min((long)a.n - 1, p + (long)dl * (s_lo + (long)kKeyTile * n_local - 1));
+      } else {
+        lo = s_lo;
+        hi = s_hi;
+      }
+      lo &= ~63L;
+      const long words = ((hi - lo) >> 6) + 1;
+      pad_staged = words <= kBwdPadWords;
+      pad_lo = (int)lo;
+      if (pad_staged) {
+        for (int w = wave; w < (int)words; w += NW) {
+          const int pos = pad_lo + 64 * w + lane;
+          const unsigned long long m = __ballot(pos < a.n && pad[pos] == 0);
+          if (lane == 0) sm.pad_bits[w] = m;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(fa[s]), "v"(fb[s]));
+    __syncthreads();
+    if (n_local == 0 && n_tiles > 0) issue(0, tile_of(0));
+
+    // bits of the global rows among the rows of window tile t (they are dropped there)
+    auto global_rows = [&](const STile& T, int t) -> unsigned long long {
+      if (n_gtiles == 0) return 0ull;
+      if (gbits_staged) return sm.g_bits[t];
+      const bool in = lane < T.count;
+      const int pos = in ? T.base + kst * lane : 0;
+      int c = -1;  // last global row with position <= pos (positions ascend)
+#pragma unroll
+      for (int step = kGlobalCap; step > 0; step >>= 1)
+        if (c + step < a.g && sm.g_pos[c + step] <= pos) c += step;
+      const bool hit = in && c >= 0 && sm.g_pos[c] == pos && ((sm.g_valid[c >> 6] >> (c & 63)) & 1ull);
+      return __ballot(hit);
+    };
+    // usable streamed rows of a local tile: they exist and (dQ) the key is not padded
+    auto local_valid = [&](const STile& T) -> unsigned long long {
+      const unsigned long long cnt = T.count >= 64 ? ~0ull : ((1ull << T.count) - 1ull);
+      if (!DQ || !pad) return cnt;
+      const bool in = lane < T.count;
+      const long pos = in ? (long)T.base + (long)kst * lane : 0;
+      bool ok;
+      if (pad_staged) {
+        const int rel = in ? (int)(pos - pad_lo) : 0;
+        ok = in && ((sm.pad_bits[rel >> 6] >> (rel & 63)) & 1ull);
+      } else {
+        ok = in && pad[pos] == 0;
+      }
+      return __ballot(ok);
+    };
+
+    // ------------------------------------------------------------------ per-lane LDS offsets
+    // Row-major A operand (streamed row 32kb + qj, k-step ks): logical chunk 2ks + hh.
+    const int swa = swz_v<D>(qj);
+    const int swb = DQ ? swz_k<D>(qj) : swz_v<D>(qj);
+    int koa[KS], kob[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      koa[ks] = qj * (2 * D) + (((2 * ks + hh) ^ swa) * 16);
+      kob[ks] = qj * (2 * D) + (((2 * ks + hh) ^ swb) * 16);
+    }
+    // Transposed A operand for 16-row group t, d block db, half r (as in the forward pass).
+    const int vi = lane & 15, vg = lane >> 4;
+    const int vrow0 = 4 * hh + (vi >> 2);
+    const int vsw = swz_v<D>(vrow0);
+    int toffs[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * (vg & 1) + ((vi & 3) >> 1);
+      toffs[db] = vrow0 * (2 * D) + ((chunk ^ vsw) * 16) + 8 * (vi & 1);
+    }
+    auto read_t = [&](const unsigned char* stg, int grp, int db) -> u32x4 {
+      const unsigned char* vp = stg + toffs[db] + 16 * grp * (2 * D);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vp + 8 * (2 * D)));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+      return u32x4{w0[0], w0[1], w1[0], w1[1]};
+    };
+
+    // ------------------------------------------------------------------ accumulators
+    // acc0: dQ^T (dQ kind) or dK^T; acc1: dV^T.  Register r of block db is d = 32db + 8(r/4) +
+    // 4hh + r%4 of the lane's owner row.
+    f32x16 acc0[DB], acc1[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[db][r] = 0.f;
+        acc1[db][r] = 0.f;
+      }
+
+    const int w_first = o0 + wave * RW;
+    const int w_last = (MODE == kBand) ? min(w_first + RW - 1, np - 1) : w_first + RW - 1;
+    bool wave_rows;
+    if constexpr (MODE == kBand) wave_rows = w_first < np;
+    else wave_rows = (rg * QT + wave * RW) < a.g;
+
+    auto reach = [&](const STile& T, bool& need_band) -> bool {
+      need_band = false;
+      if (!wave_rows) return false;
+      if constexpr (MODE == kBand) {
+        if (!T.gathered) {
+          const int kf = T.ks0, kl = T.ks0 + kKeyTile - 1;
+          if (kl < w_first - WL || kf > w_last + WR) return false;
+          need_band = !(kf >= w_last - WL && kl <= w_first + WR);
+        }
+      }
+      return true;
+    };
+
+    // ------------------------------------------------------------------ one tile
+    auto compute = [&](int si, const STile& T, unsigned long long vmask, bool need_band) {
+      const unsigned char* sa = sm.stage_a[si];
+      const unsigned char* sb = sm.stage_b[si];
+      // raw scores and dP, both C[streamed][owner]
+      f32x16 sc[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[kb][r] = 0.f;
+          dp[kb][r] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 xa = *reinterpret_cast<const u32x4*>(sa + koa[ks] + kb * 32 * (2 * D));
+          sc[kb] = mfma_32x32x16(xa, fa[ks], sc[kb]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 xb = *reinterpret_cast<const u32x4*>(sb + kob[ks] + kb * 32 * (2 * D));
+          dp[kb] = mfma_32x32x16(xb, fb[ks], dp[kb]);
+        }
+      }
+      // masks: register r of block kb is streamed row 32kb + 8(r/4) + 4hh + r%4
+      {
+        unsigned long long m = vmask >> (4 * hh);
+        if (need_band) {
+          const int lo = osub - WL - T.ks0 - 4 * hh;
+          const int hi = osub + WR - T.ks0 - 4 * hh;
+          unsigned long long bm = 0ull;
+          if (hi >= 0 && lo <= 63) {
+            const int lc = max(lo, 0), hc = min(hi, 63);
+            bm = (~0ull >> (63 - (hc - lc))) << lc;
+          }
+          m &= bm;
+        }
+        if (!own_ok && !DQ) m = 0ull;
+        if (need_band || vmask != ~0ull || (!DQ && __builtin_amdgcn_ballot_w64(!own_ok) != 0ull)) {
+          const float ninf = neg_inf();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            uint32_t w = (uint32_t)(m >> (32 * kb));
+            asm("" : "+v"(w));
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sc[kb][r] = keep_if_bit(sc[kb][r], w, 8 * (r >> 2) + (r & 3), ninf);
+          }
+        }
+      }
+      // P = 2^(c2 s - lse2), dS = P (dP - Drow); packed to bf16 as B operands
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t pk[8], dk[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float l4[4], d4[4];
+          if constexpr (DQ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              l4[e] = o_l2;
+              d4[e] = o_dr;
+            }
+          } else {
+            const int row = 32 * kb + 8 * q4 + 4 * hh;
+            const float4 L = *reinterpret_cast<const float4*>(&sm.row_l[si][row]);
+            const float4 R = *reinterpret_cast<const float4*>(&sm.row_d[si][row]);
+            l4[0] = L.x; l4[1] = L.y; l4[2] = L.z; l4[3] = L.w;
+            d4[0] = R.x; d4[1] = R.y; d4[2] = R.z; d4[3] = R.w;
+          }
+          float pe[4], de[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            pe[e] = exp2_fast(__builtin_fmaf(sc[kb][r], c2, -l4[e]));
+            de[e] = pe[e] * (dp[kb][r] - d4[e]);
+          }
+          pk[2 * q4] = pack_bf16x2(pe[0], pe[1]);
+          pk[2 * q4 + 1] = pack_bf16x2(pe[2], pe[3]);
+          dk[2 * q4] = pack_bf16x2(de[0], de[1]);
+          dk[2 * q4 + 1] = pack_bf16x2(de[2], de[3]);
+        }
+        // G^T += X^T C over the 16-row groups 2kb, 2kb+1
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {
+          const int grp = 2 * kb + gh;
+          const u32x4 bds = {dk[4 * gh], dk[4 * gh + 1], dk[4 * gh + 2], dk[4 * gh + 3]};
+          const u32x4 bp = {pk[4 * gh], pk[4 * gh + 1], pk[4 * gh + 2], pk[4 * gh + 3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            acc0[db] = mfma_32x32x16(read_t(sa, grp, db), bds, acc0[db]);  // dQ^T or dK^T
+            if constexpr (!DQ) acc1[db] = mfma_32x32x16(read_t(sb, grp, db), bp, acc1[db]);
+          }
+        }
+      }
+    };
+
+    // ------------------------------------------------------------------ tile loop
+    // Two stages per matrix; step t refills the stage of tile t-1 with tile t+1, waits for this
+    // wave's loads of tile t (tile t+1's stay in flight), then a barrier publishes tile t.
+    if (n_tiles > 0) {
+      int st = 0;
+      for (int t = 0; t < n_tiles; ++t) {
+        if (t > 0) __syncthreads();
+        const bool more = t + 1 < n_tiles;
+        if (more) issue(st ^ 1, tile_of(t + 1));
+        if (more) {
+          if (row_wave) wait_vmcnt<LPW + 1>();
+          else wait_vmcnt<LPW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
+        const STile T = tile_of(t);
+        bool need_band = false;
+        if (reach(T, need_band)) {
+          unsigned long long vmask;
+          if constexpr (MODE == kBand)
+            vmask = T.gathered ? sm.g_valid[T.base >> 6] : local_valid(T) & ~global_rows(T, t);
+          else
+            vmask = local_valid(T);
+          compute(st, T, vmask, need_band);
+        }
+        st ^= 1;
+      }
+    }
+
+    // ------------------------------------------------------------------ epilogue
+    if (opos < 0) return;
+    const float scale = a.scale;
+    if constexpr (MODE == kGlobalRows) {
+      // fp32 partial sums (unscaled); the combine adds the chunks
+      const int c = rg * QT + wave * RW + qj;
+      const long slot = (bh * a.g + c) * a.chunks + ck;
+      float* po = a.part + slot * (DQ ? D : 2 * D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * hh;
+          *reinterpret_cast<float4*>(po + d) =
+              make_float4(acc0[db][4 * rq], acc0[db][4 * rq + 1], acc0[db][4 * rq + 2],
+                          acc0[db][4 * rq + 3]);
+          if constexpr (!DQ)
+            *reinterpret_cast<float4*>(po + D + d) =
+                make_float4(acc1[db][4 * rq], acc1[db][4 * rq + 1], acc1[db][4 * rq + 2],
+                            acc1[db][4 * rq + 3]);
+        }
+    } else {
+      uint16_t* g0 = static_cast<uint16_t*>(DQ ? gp.dq : gp.dk) + (bh * a.n + opos) * D;
+      uint16_t* g1 = static_cast<uint16_t*>(gp.dv) + (bh * a.n + opos) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * hh;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc0[db][4 * rq] * scale, acc0[db][4 * rq + 1] * scale);
+          w[1] = pack_bf16x2(acc0[db][4 * rq + 2] * scale, acc0[db][4 * rq + 3] * scale);
+          *reinterpret_cast<u32x2*>(g0 + d) = w;
+          if constexpr (!DQ) {
+            u32x2 v;
+            v[0] = pack_bf16x2(acc1[db][4 * rq], acc1[db][4 * rq + 1]);
+            v[1] = pack_bf16x2(acc1[db][4 * rq + 2], acc1[db][4 * rq + 3]);
+            *reinterpret_cast<u32x2*>(g1 + d) = v;
+          }
+        }
+    }
+  };
+  if (gi >= 0) body(std::integral_constant<int, kGlobalRows>{}, gi);
+  else body(std::integral_constant<int, kBand>{}, mi);
+}
+
+// lse2 = lse * log2(e) (0 for an empty row: every edge of it is masked) and Drow = dO . O, one
+// row per 16 lanes (D/16 elements of O and of dO per lane).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(FwdArgs args, BwdArgs gp, long rows) {
+  constexpr int EPL = D / 16;  // elements per lane
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  if (row >= rows) return;
+  const uint16_t* o = static_cast<const uint16_t*>(gp.out) + row * D + l * EPL;
+  const uint16_t* g = static_cast<const uint16_t*>(gp.dout) + row * D + l * EPL;
+  float acc = 0.f;
+  if constexpr (EPL == 4) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(o), y = *reinterpret_cast<const u32x2*>(g);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      acc = __builtin_fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
+    }
+  } else {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(o), y = *reinterpret_cast<const u32x4*>(g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (l == 0) {
+    gp.drow[row] = acc;
+    const float lse = args.lse[row];
+    gp.lse2[row] = lse == -__builtin_inff() ? 0.f : lse * kLog2e;
+  }
+}
+
+// Adds the chunk partials of every global row: dQ (kind dQ) or dK and dV, and writes them.
+// One workgroup of D (dQ) or 2D (dK/dV) threads per (batch, head, global row).
+template <int D, int KIND>
+__global__ __launch_bounds__(256) void bwd_global_combine_kernel(FwdArgs args, BwdArgs gp) {
+  constexpr bool DQ = KIND == kBwdDQ;
+  constexpr int W = DQ ? D : 2 * D;
+  const FwdCore a = args;
+  const int t = threadIdx.x;
+  if (t >= W) return;
+  const long row = blockIdx.x;
+  const long bh = row / a.g;
+  const int c = (int)(row - bh * a.g);
+  const int b = (int)(bh / a.H);
+  const int pos = a.gidx[(long)b * a.g + c];
+  if (pos < 0 || pos >= a.n) return;
+  const float* po = a.part + (bh * a.g + c) * (long)a.chunks * W + t;
+  float s = 0.f;
+  for (int k = 0; k < a.chunks; ++k) s += po[(long)k * W];
+  const bool is_v = !DQ && t >= D;
+  const int col = is_v ? t - D : t;
+  uint16_t* dst = static_cast<uint16_t*>(DQ ? gp.dq : (is_v ? gp.dv : gp.dk)) +
+                  (bh * a.n + pos) * D + col;
+  *dst = __builtin_bit_cast(uint16_t, (__bf16)(is_v ? s : s * a.scale));
+}
+
+template <int D>
+hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream_t s,
+                        const LaunchEvents* ev) {
+  const long rows = (long)a.B * a.H * a.n;
+  auto timed = [&](int i, auto kernel, dim3 gr, dim3 bl, auto... xs) {
+    if (ev && (ev[i].start || ev[i].stop))
+      hipExtLaunchKernelGGL(kernel, gr, bl, 0, s, ev[i].start, ev[i].stop, 0, xs...);
+    else
+      hipLaunchKernelGGL(kernel, gr, bl, 0, s, xs...);
+  };
+  timed(0, bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), a, g, rows);
+  timed(1, attn_bwd_kernel<D, kBwdDQ>, dim3((unsigned)grid), dim3(256), a, g);
+  const long grows = (long)a.B * a.H * a.g;
+  if (grows > 0) {
+    FwdArgs a2 = a;
+    hipLaunchKernelGGL((bwd_global_combine_kernel<D, kBwdDQ>), dim3((unsigned)grows),
+                       dim3(256), 0, s, a2, g);
+  }
+  // the dK/dV partials live after the dQ partials
+  FwdArgs ak = a;
+  ak.part = a.part + (size_t)a.B * a.H * a.g * a.chunks * D;
+  timed(2, attn_bwd_kernel<D, kBwdDKV>, dim3((unsigned)grid), dim3(256), ak, g);
+  if (grows > 0)
+    hipLaunchKernelGGL((bwd_global_combine_kernel<D, kBwdDKV>), dim3((unsigned)grows),
+                       dim3(256), 0, s, ak, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, long grid, hipStream_t s,
+                           const LaunchEvents* ev) {
+  if (grid <= 0) return hipSuccess;
+  if (d == 64) return launch_bwd_d<64>(a, g, grid, s, ev);
+  if (d == 128) return launch_bwd_d<128>(a, g, grid, s, ev);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace longattn

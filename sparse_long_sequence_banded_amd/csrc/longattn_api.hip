@@ -199,14 +199,44 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // ------------------------------------------------------------------------------ backward
 namespace {
 
-// The backward pass: Drow per row, then dQ per query row and dK, dV per key column.
-longattn_status plan_backward(const longattn_desc* d, Plan* P) {
-  const longattn_status st = plan_call(d, false, P);
-  if (st != LONGATTN_OK) return st;
-  if (d->d > 256) return LONGATTN_ERR_UNSUPPORTED;
-  Plan& p = *P;
-  if ((long)p.a.B * p.a.H * p.a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
-  p.ws_bytes = p.empty ? 0 : (size_t)p.a.B * p.a.H * p.a.n * sizeof(float);
+// The backward pass.  bf16 with d in {64, 128} and no block layout runs on the matrix-core
+// kernels (same work decomposition as the forward: prep, dQ kernel, dK/dV kernel, global-row
+// combines); everything else on the per-row kernels (Drow, then dQ per query row and dK, dV per
+// key column).  Workspace: matrix-core path: Drow and lse2 per row (each padded to 4 floats) and
+// fp32 partials of the global rows (dQ: B*H*g*chunks*d; dK, dV: twice that); per-row path: Drow.
+struct BwdPlan {
+  Plan p;
+  bool mfma = false;
+  size_t rows_pad = 0;  // floats per per-row array (matrix-core path)
+};
+
+longattn_status plan_backward(const longattn_desc* d, BwdPlan* B) {
+  Plan& p = B->p;
+  bool fast = d && d->dtype == LONGATTN_BF16 && (d->d == 64 || d->d == 128) &&
+              !d->block_layout;
+  longattn_status st = LONGATTN_OK;
+  if (fast) {
+    st = plan_call(d, true, &p);
+    if (st == LONGATTN_ERR_UNSUPPORTED) fast = false;  // limits of the matrix-core kernels
+    else if (st != LONGATTN_OK) return st;
+  }
+  if (!fast) {
+    st = plan_call(d, false, &p);
+    if (st != LONGATTN_OK) return st;
+    if (d->d > 256) return LONGATTN_ERR_UNSUPPORTED;
+    if ((long)p.a.B * p.a.H * p.a.n / 4 + 1 > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  }
+  B->mfma = fast;
+  const size_t rows = (size_t)p.a.B * p.a.H * p.a.n;
+  if (p.empty) {
+    p.ws_bytes = 0;
+  } else if (fast) {
+    B->rows_pad = (rows + 3) & ~(size_t)3;
+    const size_t part = (size_t)p.a.B * p.a.H * p.a.g * p.a.chunks * (size_t)d->d;
+    p.ws_bytes = (2 * B->rows_pad + 3 * part) * sizeof(float);
+  } else {
+    p.ws_bytes = rows * sizeof(float);
+  }
   return LONGATTN_OK;
 }
 
@@ -364,21 +394,34 @@ longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entri
 
 longattn_status longattn_backward_workspace_size(const longattn_desc* desc, size_t* bytes) {
   if (!bytes) return LONGATTN_ERR_INVALID_ARG;
-  Plan p;
-  const longattn_status st = plan_backward(desc, &p);
+  BwdPlan bp;
+  const longattn_status st = plan_backward(desc, &bp);
   if (st != LONGATTN_OK) return st;
-  *bytes = p.ws_bytes;
+  *bytes = bp.p.ws_bytes;
   return LONGATTN_OK;
 }
 
-longattn_status longattn_backward(const longattn_desc* desc, const void* q, const void* k,
-                                  const void* v, const void* out, const float* lse,
-                                  const void* dout, void* dq, void* dk, void* dv,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  Plan p;
-  longattn_status st = plan_backward(desc, &p);
+longattn_status longattn_backward_marked(const longattn_desc* desc, const void* q,
+                                         const void* k, const void* v, const void* out,
+                                         const float* lse, const void* dout, void* dq, void* dk,
+                                         void* dv, void* workspace, size_t workspace_bytes,
+                                         void* stream, void* const* marks, int32_t n_marks) {
+  if (n_marks != 0 && n_marks != LONGATTN_BWD_N_MARKS) return LONGATTN_ERR_INVALID_ARG;
+  if (n_marks && !marks) return LONGATTN_ERR_INVALID_ARG;
+  BwdPlan bp;
+  longattn_status st = plan_backward(desc, &bp);
   if (st != LONGATTN_OK) return st;
-  if (p.empty) return LONGATTN_OK;
+  Plan& p = bp.p;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto ev = [&](int i) -> hipEvent_t {
+    return n_marks ? reinterpret_cast<hipEvent_t>(marks[i]) : nullptr;
+  };
+  auto mark_all = [&]() -> bool {
+    for (int i = 0; i < n_marks; ++i)
+      if (hipEventRecord(ev(i), s) != hipSuccess) return false;
+    return true;
+  };
+  if (p.empty) return mark_all() ? LONGATTN_OK : LONGATTN_ERR_HIP;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
     return LONGATTN_ERR_INVALID_ARG;
   for (const void* x : {q, k, v, out, dout, static_cast<const void*>(dq),
@@ -386,7 +429,6 @@ longattn_status longattn_backward(const longattn_desc* desc, const void* q, cons
     if (!aligned16(x)) return LONGATTN_ERR_ALIGNMENT;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return LONGATTN_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (debug_enabled()) {
     st = debug_check(desc, s);
     if (st != LONGATTN_OK) return st;
@@ -406,10 +448,33 @@ longattn_status longattn_backward(const longattn_desc* desc, const void* q, cons
   g.dk = dk;
   g.dv = dv;
   g.drow = static_cast<float*>(workspace);
+  g.lse2 = nullptr;
   const long rows = (long)a.B * a.H * a.n;
-  hipError_t e = launch_bwd_rowdot(g, rows, desc->d, p.bf16, s);
-  if (e == hipSuccess) e = launch_bwd_rowwise(a, g, desc->d, p.bf16, s);
+  hipError_t e = hipSuccess;
+  if (bp.mfma) {
+    g.lse2 = g.drow + bp.rows_pad;
+    a.part = g.drow + 2 * bp.rows_pad;
+    LaunchEvents le[3];
+    for (int i = 0; i < 3 && n_marks; ++i) le[i] = {ev(2 * i), ev(2 * i + 1)};
+    e = launch_bwd_mfma(a, g, desc->d, p.grid_main + a.grid_rows, s, n_marks ? le : nullptr);
+  } else {
+    if (n_marks && hipEventRecord(ev(0), s) != hipSuccess) return LONGATTN_ERR_HIP;
+    e = launch_bwd_rowdot(g, rows, desc->d, p.bf16, s);
+    if (e == hipSuccess && n_marks && hipEventRecord(ev(1), s) != hipSuccess) return LONGATTN_ERR_HIP;
+    if (e == hipSuccess && n_marks && hipEventRecord(ev(2), s) != hipSuccess) return LONGATTN_ERR_HIP;
+    if (e == hipSuccess) e = launch_bwd_rowwise(a, g, desc->d, p.bf16, s);
+    for (int i = 3; i < n_marks && e == hipSuccess; ++i)
+      if (hipEventRecord(ev(i), s) != hipSuccess) return LONGATTN_ERR_HIP;
+  }
   return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
+}
+
+longattn_status longattn_backward(const longattn_desc* desc, const void* q, const void* k,
+                                  const void* v, const void* out, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return longattn_backward_marked(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace,
+                                  workspace_bytes, stream, nullptr, 0);
 }
 
 longattn_status longattn_decode_workspace_size(const longattn_decode_desc* desc, size_t* bytes) {

@@ -271,3 +271,19 @@ def test_backward_workspace_and_pointer_checks():
         assert la.longattn_backward(d, *bad, FAKE, nbytes, None) == la.LONGATTN_ERR_ALIGNMENT
     assert la.longattn_backward_workspace_size(_desc(n=0)) == (la.LONGATTN_OK, 0)
     assert la.longattn_backward(_desc(n=0), *([None] * 9), None, 0, None) == la.LONGATTN_OK
+
+
+def test_backward_matrix_core_workspace_formula():
+    # bf16, d in {64, 128}, no layout: Drow and lse2 per row (padded to 4 floats each) plus the
+    # global rows' partials: 3 * B*H*g*chunks*d floats (chunks of 1024 rows)
+    d = _desc(batch=2, heads=3, n=1001, d=64, n_global=5, global_idx=FAKE)
+    rows_pad = (2 * 3 * 1001 + 3) // 4 * 4
+    assert la.longattn_backward_workspace_size(d) == (la.LONGATTN_OK,
+                                                      (2 * rows_pad + 3 * 2 * 3 * 5 * 1 * 64) * 4)
+    d = _desc(batch=1, heads=2, n=3000, d=128)
+    assert la.longattn_backward_workspace_size(d) == (la.LONGATTN_OK, 2 * 6000 * 4)
+    # a layout (or another head dim) takes the per-row kernels: one float per row
+    dl = _desc(block_layout=FAKE, block=64, max_kb=2, win_left=-1, win_right=-1)
+    assert la.longattn_backward_workspace_size(dl) == (la.LONGATTN_OK, 2 * 256 * 4)
+    assert la.longattn_backward_marked(_desc(), *([FAKE] * 9), FAKE, 1 << 30, None,
+                                       [FAKE] * 3) == la.LONGATTN_ERR_INVALID_ARG
