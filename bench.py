@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --decode swa512_decode_32k [--steps K] [--warmup W]
+    python bench.py --backward [--workload NAME] [--steps K] [--warmup W]
 
 One step is one full forward pass (global-row partials, main sparse kernel, global-row combine)
 over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
@@ -40,6 +41,9 @@ def _parse():
     ap.add_argument("--decode", default=None, metavar="NAME",
                     help="instead of the forward bench: time decode steps of the named decode "
                          "workload (swa512_decode_32k), an HBM-bound path, reported in GB/s")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward bench: time the backward pass (dQ, dK, dV from "
+                         "the saved out and lse) of the workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the attention bench: time K device-to-device copies of this "
                          "many MiB (a kernel of known HBM traffic, used to calibrate the "
@@ -159,6 +163,122 @@ def _decode_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _backward_bench(args):
+    """Backward steps: useful TFLOP/s = 10*d*E / step time (per allowed entry: the score, dP, dQ,
+    dK and dV products, 2d flops each; the kernels recompute the score and dP once more)."""
+    import numpy as np
+    import torch
+
+    import sparse_long_sequence_banded_amd as la
+    from workloads import draw_dout, make_inputs, workload
+    from workloads.torch_io import to_torch
+
+    w = workload(args.workload)
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    t = to_torch(inp, dev)
+    q, k, v = t["q"], t["k"], t["v"]
+    kw = dict(scale=inp.scale, win_left=inp.win_left, win_right=inp.win_right,
+              dilation=inp.dilation, global_idx=t["global_idx"], key_pad=t["key_pad"],
+              block_layout=t["layout"], block=inp.block)
+    E, _ = la.count_entries(q, **{k2: kw[k2] for k2 in kw if k2 != "scale"})
+    out, lse = la.forward(q, k, v, **kw)
+    g = draw_dout(inp, 1)
+    dout = (torch.from_numpy(g.view(np.int16)).view(torch.bfloat16) if inp.dtype == "bf16"
+            else torch.from_numpy(g)).to(dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    desc, keep = la.make_desc(q, **kw)
+    _, ws_bytes = la.longattn_backward_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+            ws_bytes, stream.cuda_stream)
+
+    def step(marks=None):
+        st = (la.longattn_backward(desc, *ptrs) if marks is None
+              else la.longattn_backward_marked(desc, *ptrs, marks))
+        if st != la.LONGATTN_OK:
+            raise la.LongAttnError(st, "longattn_backward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(la.LONGATTN_BWD_N_MARKS)]
+             for _ in range(args.steps)]
+    for row in marks:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        step([e.cuda_event for e in marks[s_]])
+    torch.cuda.synchronize()
+    spans = np.array([[marks[s_][2 * i].elapsed_time(marks[s_][2 * i + 1]) for i in range(3)]
+                      for s_ in range(args.steps)]).mean(axis=0)
+    prep_ms, dq_ms, dkv_ms = (float(x) for x in spans)
+    useful = 10.0 * inp.d * E
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    # per-kernel useful work: the dQ kernel does the score, dP and dQ products (6d per entry),
+    # the dK/dV kernel the score, dP, dK and dV products (8d per entry)
+    dq_tf = 6.0 * inp.d * E / (dq_ms * 1e-3) / 1e12
+    dkv_tf = 8.0 * inp.d * E / (dkv_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "useful TFLOP/s of the backward pass (10*d*E per step), window attn at "
+                  "n=4096/16384 (1 GPU)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": inp.batch, "heads": inp.heads, "seq_len": inp.n,
+                   "head_dim": inp.d, "useful_entries": E, "description": w.note},
+        "pct_bf16_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernels_ms": {"prep": round(prep_ms, 5), "dq": round(dq_ms, 5),
+                       "dkdv": round(dkv_ms, 5)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bwd_kernel dK/dV kind (score, dP, dK, dV products: 8*d*E)",
+            "achieved": round(dkv_tf, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dkv_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "roofline_dq": {"achieved": round(dq_tf, 3), "frac": round(dq_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from workloads import widen
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        sub = inp.select_heads([0])
+        t0 = time.perf_counter()
+        oracle.backward_inputs(sub, widen(np.ascontiguousarray(g[:, :1]), inp.dtype),
+                               nthreads=threads)
+        dt = time.perf_counter() - t0
+        E1 = oracle.count_inputs(sub)
+        rec["cpu_baseline"] = {
+            "value": round(10.0 * inp.d * E1 / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(threads, inp.batch), "kind": "oracle",
+            "sample": f"head 0 of {inp.heads} (all rows; the oracle runs one thread per (b, h)), "
+                      f"{E1} entries, {dt:.2f} s"}
+    else:
+        rec["cpu_baseline"] = None
+    del keep
+    print(json.dumps(rec), flush=True)
+
+
 def _source_hash():
     with open(MAIN_KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -220,6 +340,9 @@ def main():
         return
     if args.decode:
         _decode_bench(args)
+        return
+    if args.backward:
+        _backward_bench(args)
         return
 
     import numpy as np

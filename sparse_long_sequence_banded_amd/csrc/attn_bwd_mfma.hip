@@ -1,4 +1,5 @@
-// bf16 backward pass of the window / dilation / global-token pattern on gfx950 matrix cores.
+// bf16 backward pass of the window / dilation / global-token and block-layout patterns on gfx950
+// matrix cores.
 //
 // With the forward's log-normaliser of every query row (kept in log2 units, lse2), the softmax
 // weights of an edge are recomputed directly, P = 2^(c2 s - lse2), c2 = scale * log2(e), so no
@@ -25,6 +26,11 @@
 // (batch, head, 128 global rows, 1024-row chunk), which stream every position of the chunk and
 // write fp32 partial sums; a combine kernel adds the chunks and overwrites those rows.
 //
+// Block layouts (Big Bird reading notes, sections 3.2.2 and 3.3): a dQ workgroup owns a query
+// block and streams its listed key blocks; a dK/dV workgroup owns a key block and streams the
+// query blocks whose layout rows list it (found by scanning the layout).  As in the forward pass,
+// a global key inside a listed block is attended through the block.
+//
 // Wave-level math (32x32x16 bf16 MFMA, fp32 accumulate).  Scores come out as C[streamed row]
 // [owner row]: every lane holds one owner row (its column) against 32 streamed rows.  The
 // gradient sums are kept transposed, G^T[d][owner] += X^T[d][streamed] C[streamed][owner], so
@@ -46,6 +52,7 @@ using namespace mfma;
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kBwdPadWords = 64;  // staged key-padding and global-row bits: 4096 positions
+constexpr int kBwdMaxBlocks = 1024;  // layout mode: listed (or listing) blocks per workgroup
 
 template <int D>
 struct BwdSmem {
@@ -57,6 +64,9 @@ struct BwdSmem {
   unsigned long long g_valid[kGlobalCap / 64];             // global rows: usable bits
   unsigned long long g_bits[kBwdPadWords];                 // global rows among window rows
   unsigned long long pad_bits[kBwdPadWords];               // dQ: key padding of window keys
+  int lay_list[kBwdMaxBlocks];  // layout mode: streamed blocks (dQ: listed key blocks of the
+                                // query block; dK/dV: query blocks that list the key block)
+  int lay_cnt;
 };
 
 struct STile {
@@ -66,8 +76,8 @@ struct STile {
   int ks0;       // window tiles: residue-subsequence index of row 0
 };
 
-template <int D, int KIND>
-__global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
+template <int D, int KIND, int NW, int MODE_MAIN>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
   __shared__ BwdSmem<D> sm;
   const FwdCore a = args;
   const BwdArgs gp = gargs;
@@ -103,16 +113,17 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
   auto body = [&](auto mode_c, const int wg) {
     constexpr int MODE = decltype(mode_c)::value;
     constexpr bool DQ = KIND == kBwdDQ;
-    constexpr int NW = 4, NT = 256, RW = 32, QT = NW * RW;
+    constexpr int NT = NW * 64, RW = 32, QT = NW * RW;
     constexpr int CH = D / 8;          // 16-byte chunks per row
     constexpr int KS = D / 16;         // MFMA k-steps over the head dim
     constexpr int DB = D / 32;         // 32-row blocks of a transposed gradient
     constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (matrix A, then B)
     constexpr int LPW = NLOAD / NW;
     constexpr int RPB = 64 / CH;       // rows per 1 KB block
-    constexpr bool kGathered = MODE == kBand;  // window workgroups also walk the global rows
+    constexpr bool kGathered = MODE != kGlobalRows;  // main workgroups also walk the global rows
+    constexpr int GREG = kGlobalCap / NT;            // global rows staged per thread
     static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
-    static_assert(kGlobalCap == NT, "one global row per thread when staging");
+    static_assert(kGlobalCap % NT == 0, "whole rounds of global rows when staging");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -137,14 +148,16 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
       h = main_h;
       dl = main_dl;
       int r = main_r;
-      for (;;) {  // residue class p holds ceil((n - p) / dl) positions
-        const int n_p = (a.n - p + dl - 1) / dl;
-        const int t_p = (n_p + QT - 1) / QT;
-        if (r < t_p) { np = n_p; break; }
-        r -= t_p;
-        ++p;
+      if constexpr (MODE == kBand) {
+        for (;;) {  // residue class p holds ceil((n - p) / dl) positions
+          const int n_p = (a.n - p + dl - 1) / dl;
+          const int t_p = (n_p + QT - 1) / QT;
+          if (r < t_p) { np = n_p; break; }
+          r -= t_p;
+          ++p;
+        }
       }
-      o0 = r * QT;
+      o0 = r * QT;  // kLayout: block r (QT == block)
     }
     const int kst = (MODE == kBand) ? min(dl, a.n) : 1;
     const long bh = (long)b * a.H + h;
@@ -165,6 +178,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
       if constexpr (MODE == kBand) {
         osub = o0 + orow;
         if (osub < np) opos = p + dl * osub;
+      } else if constexpr (MODE == kLayout) {
+        osub = o0 + orow;
+        opos = osub;
       } else {
         const int c = rg * QT + orow;
         if (c < a.g) {
@@ -174,8 +190,43 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
       }
     }
     // ------------------------------------------------------------------ streamed tiles
-    int n_local = 0, s_lo = 0, s_hi = -1;
-    if constexpr (MODE == kBand) {
+    int n_local = 0, s_lo = 0, s_hi = -1, tpb = 1;
+    if constexpr (MODE == kLayout) {
+      // dQ: the valid key blocks listed for this query block; dK/dV: the query blocks whose
+      // layout row lists this key block, in ascending order (compacted by wave 0)
+      tpb = a.block / kKeyTile;
+      const int nb = a.n / a.block;
+      const int me = o0 / a.block;
+      if (wave == 0) {
+        int base = 0;
+        if constexpr (DQ) {
+          const int* row = a.layout + ((long)h * nb + me) * a.max_kb;
+          for (int e0 = 0; e0 < a.max_kb; e0 += 64) {
+            const int e = e0 + lane;
+            int id = (e < a.max_kb) ? row[e] : -1;
+            if (id >= nb) id = -1;  // out-of-range ids are ignored rather than read
+            const unsigned long long m = __ballot(id >= 0);
+            if (id >= 0) sm.lay_list[base + __popcll(m & ((1ull << lane) - 1ull))] = id;
+            base += __popcll(m);
+          }
+        } else {
+          for (int q0b = 0; q0b < nb; q0b += 64) {
+            const int qb = q0b + lane;
+            bool lists = false;
+            if (qb < nb) {
+              const int* row = a.layout + ((long)h * nb + qb) * a.max_kb;
+              for (int e = 0; e < a.max_kb; ++e) lists = lists | (row[e] == me);
+            }
+            const unsigned long long m = __ballot(lists);
+            if (lists) sm.lay_list[base + __popcll(m & ((1ull << lane) - 1ull))] = qb;
+            base += __popcll(m);
+          }
+        }
+        if (lane == 0) sm.lay_cnt = base;
+      }
+      __syncthreads();
+      n_local = sm.lay_cnt * tpb;
+    } else if constexpr (MODE == kBand) {
       if (a.band_on) {
         const int o_last = min(o0 + QT, np) - 1;
         s_lo = max(0, o0 - WL);
@@ -204,6 +255,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
         T.ks0 = s_lo + t * kKeyTile;
         T.base = p + dl * T.ks0;
         T.count = min(kKeyTile, np - T.ks0);
+      } else if constexpr (MODE == kLayout) {
+        T.gathered = 0;
+        T.base = sm.lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
+        T.count = kKeyTile;
       } else {
         T.gathered = 0;
         T.base = s_lo + t * kKeyTile;
@@ -260,8 +315,12 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
 
     // Global rows first (positions feed the gathered tiles and the window-tile exclusion), then
     // the first window tile, the owner fragments and the staging.
-    int gx = a.n;
-    if (kGathered && n_gtiles > 0 && tid < a.g) gx = gb[tid];
+    int gx[GREG];
+#pragma unroll
+    for (int i = 0; i < GREG; ++i) {
+      const int c = tid + NT * i;
+      gx[i] = (kGathered && n_gtiles > 0 && c < a.g) ? gb[c] : a.n;
+    }
     if (n_local > 0) issue(0, tile_of(0));
 
     // Owner fragments (B operands): lane (qj, hh) holds d = 16ks + 8hh .. +7 of its owner row.
@@ -291,27 +350,38 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
     // Usable global rows: dQ streams global keys (in range, not padded); dK/dV streams global
     // query rows (in range).  Window tiles drop them (g_bits over the window range when it fits,
     // else a search of the sorted positions).
-    const bool gbits_staged = kGathered && n_gtiles > 0 && n_local <= kBwdPadWords;
+    const bool gbits_staged = MODE == kBand && n_gtiles > 0 && n_local <= kBwdPadWords;
     if constexpr (kGathered) {
       if (n_gtiles > 0) {
         if (gbits_staged) {
           for (int w = tid; w < n_local; w += NT) sm.g_bits[w] = 0ull;
           __syncthreads();
         }
-        const int x = gx;
-        bool ok = tid < a.g && x >= 0 && x < a.n;
-        if constexpr (DQ) {
-          if (ok && pad) ok = pad[x] == 0;
+#pragma unroll
+        for (int i = 0; i < GREG; ++i) {
+          const int c = tid + NT * i;
+          const int x = gx[i];
+          bool ok = c < a.g && x >= 0 && x < a.n;
+          if constexpr (DQ) {
+            if (ok && pad) ok = pad[x] == 0;
+          }
+          const int pos = min(max(x, 0), a.n);
+          if constexpr (DQ && MODE == kLayout) {
+            // a global key inside one of the listed blocks is attended through the block
+            const int blk = pos / a.block;
+            for (int e = 0; e < sm.lay_cnt; ++e) ok = ok && (sm.lay_list[e] != blk);
+          }
+          if constexpr (MODE == kBand) {
+            const int rel = pos - p;
+            if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
+              const int j = rel / dl - s_lo;
+              if (j >= 0 && j < kKeyTile * n_local) atomicOr(&sm.g_bits[j >> 6], 1ull << (j & 63));
+            }
+          }
+          sm.g_pos[c] = pos;
+          const unsigned long long vm = __ballot(ok);
+          if (lane == 0) sm.g_valid[c >> 6] = vm;
         }
-        const int pos = min(max(x, 0), a.n);
-        const int rel = pos - p;
-        if (gbits_staged && ok && rel >= 0 && rel % dl == 0) {
-          const int j = rel / dl - s_lo;
-          if (j >= 0 && j < kKeyTile * n_local) atomicOr(&sm.g_bits[j >> 6], 1ull << (j & 63));
-        }
-        sm.g_pos[tid] = pos;
-        const unsigned long long vm = __ballot(ok);
-        if (lane == 0) sm.g_valid[tid >> 6] = vm;
       }
     }
     // dQ: key padding of the reachable window positions as bits, when they fit.
@@ -322,6 +392,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
       if constexpr (MODE == kBand) {
         lo = p + (long)dl * s_lo;
         hi = min((long)a.n - 1, p + (long)dl * (s_lo + (long)kKeyTile * n_local - 1));
+      } else if constexpr (MODE == kLayout) {
+        lo = 0;
+        hi = a.n - 1;
       } else {
         lo = s_lo;
         hi = s_hi;
@@ -416,6 +489,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
     const int w_last = (MODE == kBand) ? min(w_first + RW - 1, np - 1) : w_first + RW - 1;
     bool wave_rows;
     if constexpr (MODE == kBand) wave_rows = w_first < np;
+    else if constexpr (MODE == kLayout) wave_rows = true;
     else wave_rows = (rg * QT + wave * RW) < a.g;
 
     auto reach = [&](const STile& T, bool& need_band) -> bool {
@@ -547,9 +621,15 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
         const STile T = tile_of(t);
         bool need_band = false;
         if (reach(T, need_band)) {
+          // window tiles drop the global rows (they go through the global paths); listed layout
+          // blocks keep global keys (dQ: the global column skips them) but drop global query
+          // rows (dK/dV: those rows are streamed from the global list)
           unsigned long long vmask;
           if constexpr (MODE == kBand)
             vmask = T.gathered ? sm.g_valid[T.base >> 6] : local_valid(T) & ~global_rows(T, t);
+          else if constexpr (MODE == kLayout)
+            vmask = T.gathered ? sm.g_valid[T.base >> 6]
+                               : (DQ ? local_valid(T) : local_valid(T) & ~global_rows(T, t));
           else
             vmask = local_valid(T);
           compute(st, T, vmask, need_band);
@@ -601,7 +681,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(FwdArgs args, BwdArgs gar
     }
   };
   if (gi >= 0) body(std::integral_constant<int, kGlobalRows>{}, gi);
-  else body(std::integral_constant<int, kBand>{}, mi);
+  else body(std::integral_constant<int, MODE_MAIN>{}, mi);
 }
 
 // lse2 = lse * log2(e) (0 for an empty row: every edge of it is masked) and Drow = dO . O, one
@@ -664,7 +744,7 @@ __global__ __launch_bounds__(256) void bwd_global_combine_kernel(FwdArgs args, B
   *dst = __builtin_bit_cast(uint16_t, (__bf16)(is_v ? s : s * a.scale));
 }
 
-template <int D>
+template <int D, int NW, int MODE>
 hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream_t s,
                         const LaunchEvents* ev) {
   const long rows = (long)a.B * a.H * a.n;
@@ -675,7 +755,7 @@ hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream
       hipLaunchKernelGGL(kernel, gr, bl, 0, s, xs...);
   };
   timed(0, bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), a, g, rows);
-  timed(1, attn_bwd_kernel<D, kBwdDQ>, dim3((unsigned)grid), dim3(256), a, g);
+  timed(1, attn_bwd_kernel<D, kBwdDQ, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), a, g);
   const long grows = (long)a.B * a.H * a.g;
   if (grows > 0) {
     FwdArgs a2 = a;
@@ -685,7 +765,7 @@ hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream
   // the dK/dV partials live after the dQ partials
   FwdArgs ak = a;
   ak.part = a.part + (size_t)a.B * a.H * a.g * a.chunks * D;
-  timed(2, attn_bwd_kernel<D, kBwdDKV>, dim3((unsigned)grid), dim3(256), ak, g);
+  timed(2, attn_bwd_kernel<D, kBwdDKV, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), ak, g);
   if (grows > 0)
     hipLaunchKernelGGL((bwd_global_combine_kernel<D, kBwdDKV>), dim3((unsigned)grows),
                        dim3(256), 0, s, ak, g);
@@ -694,11 +774,19 @@ hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream
 
 }  // namespace
 
-hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, long grid, hipStream_t s,
-                           const LaunchEvents* ev) {
+hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, int mode, long grid,
+                           hipStream_t s, const LaunchEvents* ev) {
   if (grid <= 0) return hipSuccess;
-  if (d == 64) return launch_bwd_d<64>(a, g, grid, s, ev);
-  if (d == 128) return launch_bwd_d<128>(a, g, grid, s, ev);
+  if (mode == kBand) {
+    if (d == 64) return launch_bwd_d<64, 4, kBand>(a, g, grid, s, ev);
+    if (d == 128) return launch_bwd_d<128, 4, kBand>(a, g, grid, s, ev);
+  } else if (mode == kLayout && a.block == 64) {
+    if (d == 64) return launch_bwd_d<64, 2, kLayout>(a, g, grid, s, ev);
+    if (d == 128) return launch_bwd_d<128, 2, kLayout>(a, g, grid, s, ev);
+  } else if (mode == kLayout && a.block == 128) {
+    if (d == 64) return launch_bwd_d<64, 4, kLayout>(a, g, grid, s, ev);
+    if (d == 128) return launch_bwd_d<128, 4, kLayout>(a, g, grid, s, ev);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -199,8 +199,8 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // ------------------------------------------------------------------------------ backward
 namespace {
 
-// The backward pass.  bf16 with d in {64, 128} and no block layout runs on the matrix-core
-// kernels (same work decomposition as the forward: prep, dQ kernel, dK/dV kernel, global-row
+// The backward pass.  bf16 with d in {64, 128} (window or layout, within the forward's bf16
+// limits and at most 1024 layout blocks) runs on the matrix-core kernels (same work decomposition as the forward: prep, dQ kernel, dK/dV kernel, global-row
 // combines); everything else on the per-row kernels (Drow, then dQ per query row and dK, dV per
 // key column).  Workspace: matrix-core path: Drow and lse2 per row (each padded to 4 floats) and
 // fp32 partials of the global rows (dQ: B*H*g*chunks*d; dK, dV: twice that); per-row path: Drow.
@@ -213,7 +213,7 @@ struct BwdPlan {
 longattn_status plan_backward(const longattn_desc* d, BwdPlan* B) {
   Plan& p = B->p;
   bool fast = d && d->dtype == LONGATTN_BF16 && (d->d == 64 || d->d == 128) &&
-              !d->block_layout;
+              (!d->block_layout || (d->block > 0 && d->n / d->block <= kBwdMaxLayoutBlocks));
   longattn_status st = LONGATTN_OK;
   if (fast) {
     st = plan_call(d, true, &p);
@@ -456,7 +456,8 @@ longattn_status longattn_backward_marked(const longattn_desc* desc, const void* 
     a.part = g.drow + 2 * bp.rows_pad;
     LaunchEvents le[3];
     for (int i = 0; i < 3 && n_marks; ++i) le[i] = {ev(2 * i), ev(2 * i + 1)};
-    e = launch_bwd_mfma(a, g, desc->d, p.grid_main + a.grid_rows, s, n_marks ? le : nullptr);
+    e = launch_bwd_mfma(a, g, desc->d, p.mode, p.grid_main + a.grid_rows, s,
+                        n_marks ? le : nullptr);
   } else {
     if (n_marks && hipEventRecord(ev(0), s) != hipSuccess) return LONGATTN_ERR_HIP;
     e = launch_bwd_rowdot(g, rows, desc->d, p.bf16, s);

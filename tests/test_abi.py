@@ -282,8 +282,13 @@ def test_backward_matrix_core_workspace_formula():
                                                       (2 * rows_pad + 3 * 2 * 3 * 5 * 1 * 64) * 4)
     d = _desc(batch=1, heads=2, n=3000, d=128)
     assert la.longattn_backward_workspace_size(d) == (la.LONGATTN_OK, 2 * 6000 * 4)
-    # a layout (or another head dim) takes the per-row kernels: one float per row
+    # a layout of 64- or 128-blocks alone also runs on matrix cores ...
     dl = _desc(block_layout=FAKE, block=64, max_kb=2, win_left=-1, win_right=-1)
-    assert la.longattn_backward_workspace_size(dl) == (la.LONGATTN_OK, 2 * 256 * 4)
+    assert la.longattn_backward_workspace_size(dl) == (la.LONGATTN_OK, 2 * 512 * 4)
+    # ... a layout together with a window, other head dims or fp32 take the per-row kernels:
+    # one float per row
+    dw = _desc(block_layout=FAKE, block=64, max_kb=2)
+    assert la.longattn_backward_workspace_size(dw) == (la.LONGATTN_OK, 2 * 256 * 4)
+    assert la.longattn_backward_workspace_size(_desc(d=96)) == (la.LONGATTN_OK, 2 * 256 * 4)
     assert la.longattn_backward_marked(_desc(), *([FAKE] * 9), FAKE, 1 << 30, None,
                                        [FAKE] * 3) == la.LONGATTN_ERR_INVALID_ARG

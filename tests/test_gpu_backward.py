@@ -150,6 +150,15 @@ def test_random_shapes_backward_parity(case):
     check(random_case(**case), case["seed"], str(case["seed"]))
 
 
+@pytest.mark.parametrize("block,d", [(64, 128), (128, 64), (128, 128)])
+def test_layout_backward_with_globals_and_padding(block, d):
+    """Block layouts on the matrix-core path: listed blocks, global tokens inside and outside
+    the listed blocks, key padding."""
+    inp = random_case(78 + block + d, batch=2, heads=2, n=block * 9, d=d, block=block, max_kb=3,
+                      n_global=21, pad="random", pad_count=40)
+    check(inp, 78, f"layout block {block} d{d}")
+
+
 # ------------------------------------------------------------------------------ edge cases
 def test_window_zero_sends_the_gradient_to_v():
     inp = random_case(75, batch=2, heads=2, n=300, d=64, win_left=0, win_right=0,
