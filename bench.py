@@ -220,7 +220,7 @@ def _backward_bench(args):
     torch.cuda.synchronize()
     spans = np.array([[marks[s_][2 * i].elapsed_time(marks[s_][2 * i + 1]) for i in range(3)]
                       for s_ in range(args.steps)]).mean(axis=0)
-    prep_ms, dq_ms, dkv_ms = (float(x) for x in spans)
+    dq_ms, dkv_ms, comb_ms = (float(x) for x in spans)
     useful = 10.0 * inp.d * E
     value = useful / (ms_per_step * 1e-3) / 1e12
     # per-kernel useful work: the dQ kernel does the score, dP and dQ products (6d per entry),
@@ -244,8 +244,8 @@ def _backward_bench(args):
         "config": {"workload": w.name, "batch": inp.batch, "heads": inp.heads, "seq_len": inp.n,
                    "head_dim": inp.d, "useful_entries": E, "description": w.note},
         "pct_bf16_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-        "kernels_ms": {"prep": round(prep_ms, 5), "dq": round(dq_ms, 5),
-                       "dkdv": round(dkv_ms, 5)},
+        "kernels_ms": {"dq": round(dq_ms, 5), "dkdv": round(dkv_ms, 5),
+                       "global_combine": round(comb_ms, 5)},
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_bwd_kernel dK/dV kind (score, dP, dK, dV products: 8*d*E)",

@@ -141,11 +141,12 @@ longattn_status longattn_backward(const longattn_desc* desc, const void* q, cons
                                   const void* dout, void* dq, void* dk, void* dv,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* The same pass with caller-created hipEvent_t handles that time its phases: marks[0..1] the
- * start and end of the row preparation (Drow, lse in log2 units), marks[2..3] of the dQ kernel,
- * marks[4..5] of the dK/dV kernel (matrix-core path: attached to the kernels' dispatches; the
- * global-row combines fall outside them).  On the per-row path marks[0..1] bracket Drow and
- * marks[2..5] the dQ and dK/dV kernels together.  n_marks: 0 or LONGATTN_BWD_N_MARKS. */
+/* The same pass with caller-created hipEvent_t handles that time its phases.  Matrix-core path
+ * (attached to the kernels' dispatches): marks[0..1] the start and end of the dQ kernel (which
+ * also prepares each row's Drow), marks[2..3] of the dK/dV kernel, marks[4..5] of the global-
+ * token combine (recorded back to back when there are no global tokens).  Per-row path:
+ * marks[0..1] bracket the Drow kernel and marks[2..5] the dQ and dK/dV kernels together.
+ * n_marks: 0 or LONGATTN_BWD_N_MARKS. */
 #define LONGATTN_BWD_N_MARKS 6
 longattn_status longattn_backward_marked(const longattn_desc* desc, const void* q,
                                          const void* k, const void* v, const void* out,

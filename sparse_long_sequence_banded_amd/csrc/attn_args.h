@@ -101,7 +101,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& g, long rows, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_rowwise(const FwdArgs& a, const BwdArgs& g, int d, bool bf16,
                               hipStream_t s);
-// ev: null or three start/stop pairs (prep, dQ kernel, dK/dV kernel)
+// ev: null or three start/stop pairs (dQ kernel, dK/dV kernel, global-token combine)
 hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, int mode, long grid,
                            hipStream_t s, const LaunchEvents* ev);
 constexpr int kBwdMaxLayoutBlocks = 1024;  // matrix-core backward: n / block limit

@@ -7,9 +7,10 @@
 //   dP = dO_i . v_j,  dS = P (dP - Drow_i),
 //   dQ_i += scale * dS k_j,  dK_j += scale * dS q_i,  dV_j += P dO_i.
 // Every gradient row has one owner, so there are no atomics.  Two launches of one kernel
-// template:
+// template (then one combine for the global tokens):
 //   dQ kind:   a wave owns 32 query rows (its Q and dO rows are MFMA B operands held in
 //              registers) and streams 64-key tiles of K and V through LDS, like the forward pass;
+//              it also computes every row's Drow and lse2 once and stores them for the next;
 //   dK/dV kind: a wave owns 32 key rows (K and V rows in registers) and streams 64-row tiles of
 //              Q and dO through LDS, with each streamed row's lse2 and Drow.
 // In both, the streamed rows s of owner row o satisfy o - WL <= s <= o + WR in the residue
@@ -335,12 +336,36 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(FwdArgs args, BwdArgs
         fb[s] = *reinterpret_cast<const u32x4*>(OB + (long)opos * D + 16 * s + 8 * hh);
       }
     }
-    float o_l2 = 0.f, o_dr = 0.f;  // dQ: the owner query's lse2 and Drow
-    bool own_ok = opos >= 0;       // dK/dV: the owner key exists and is not padded
+    // dQ: the owner query's lse2 (lse in log2 units; 0 for an empty row, whose edges are all
+    // masked) and Drow = dO . O (this lane's half of the head dim, then the partner lane's);
+    // the main workgroups own every row once and leave both for the dK/dV kernel.
+    float o_l2 = 0.f, o_dr = 0.f;
+    bool own_ok = opos >= 0;  // dK/dV: the owner key exists and is not padded
     if constexpr (DQ) {
-      if (opos >= 0) {
-        o_l2 = l2b[opos];
-        o_dr = drb[opos];
+      float lse = 0.f;
+      u32x4 of[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        of[s] = u32x4{0, 0, 0, 0};
+        if (opos >= 0)
+          of[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(gp.out) +
+                                                  (bh * a.n + opos) * D + 16 * s + 8 * hh);
+      }
+      if (opos >= 0) lse = a.lse[bh * a.n + opos];
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part = __builtin_fmaf(__uint_as_float(of[s][e] << 16), __uint_as_float(fb[s][e] << 16), part);
+          part = __builtin_fmaf(__uint_as_float(of[s][e] & 0xffff0000u),
+                                __uint_as_float(fb[s][e] & 0xffff0000u), part);
+        }
+      o_dr = part + __shfl_xor(part, 32);
+      o_l2 = lse == -__builtin_inff() ? 0.f : lse * kLog2e;
+      if (MODE != kGlobalRows && opos >= 0 && hh == 0) {
+        gp.drow[bh * a.n + opos] = o_dr;
+        gp.lse2[bh * a.n + opos] = o_l2;
       }
     } else {
       if (own_ok && pad) own_ok = pad[opos] == 0;
@@ -684,91 +709,52 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(FwdArgs args, BwdArgs
   else body(std::integral_constant<int, MODE_MAIN>{}, mi);
 }
 
-// lse2 = lse * log2(e) (0 for an empty row: every edge of it is masked) and Drow = dO . O, one
-// row per 16 lanes (D/16 elements of O and of dO per lane).
+// Adds the chunk partials of every global token and writes its dQ row (the global query row)
+// and its dK and dV rows (the global key): one workgroup of 3D threads per (batch, head, global
+// token); thread t sums column t % D of one of the three over the chunks.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(FwdArgs args, BwdArgs gp, long rows) {
-  constexpr int EPL = D / 16;  // elements per lane
-  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l = threadIdx.x & 15;
-  if (row >= rows) return;
-  const uint16_t* o = static_cast<const uint16_t*>(gp.out) + row * D + l * EPL;
-  const uint16_t* g = static_cast<const uint16_t*>(gp.dout) + row * D + l * EPL;
-  float acc = 0.f;
-  if constexpr (EPL == 4) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(o), y = *reinterpret_cast<const u32x2*>(g);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      acc = __builtin_fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
-    }
-  } else {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(o), y = *reinterpret_cast<const u32x4*>(g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = __builtin_fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (l == 0) {
-    gp.drow[row] = acc;
-    const float lse = args.lse[row];
-    gp.lse2[row] = lse == -__builtin_inff() ? 0.f : lse * kLog2e;
-  }
-}
-
-// Adds the chunk partials of every global row: dQ (kind dQ) or dK and dV, and writes them.
-// One workgroup of D (dQ) or 2D (dK/dV) threads per (batch, head, global row).
-template <int D, int KIND>
-__global__ __launch_bounds__(256) void bwd_global_combine_kernel(FwdArgs args, BwdArgs gp) {
-  constexpr bool DQ = KIND == kBwdDQ;
-  constexpr int W = DQ ? D : 2 * D;
+__global__ __launch_bounds__(3 * D) void bwd_global_combine_kernel(FwdArgs args, BwdArgs gp) {
   const FwdCore a = args;
   const int t = threadIdx.x;
-  if (t >= W) return;
   const long row = blockIdx.x;
   const long bh = row / a.g;
   const int c = (int)(row - bh * a.g);
   const int b = (int)(bh / a.H);
   const int pos = a.gidx[(long)b * a.g + c];
   if (pos < 0 || pos >= a.n) return;
-  const float* po = a.part + (bh * a.g + c) * (long)a.chunks * W + t;
+  const int which = t / D, col = t % D;  // 0: dQ, 1: dK, 2: dV
+  const long slots = (long)a.B * a.H * a.g * a.chunks;
+  const long slot0 = (bh * a.g + c) * a.chunks;
+  const float* po = which == 0 ? a.part + slot0 * D + col
+                               : a.part + slots * D + slot0 * 2 * D + (which - 1) * D + col;
+  const long stride = which == 0 ? D : 2 * D;
   float s = 0.f;
-  for (int k = 0; k < a.chunks; ++k) s += po[(long)k * W];
-  const bool is_v = !DQ && t >= D;
-  const int col = is_v ? t - D : t;
-  uint16_t* dst = static_cast<uint16_t*>(DQ ? gp.dq : (is_v ? gp.dv : gp.dk)) +
+  for (int k = 0; k < a.chunks; ++k) s += po[k * stride];
+  uint16_t* dst = static_cast<uint16_t*>(which == 0 ? gp.dq : which == 1 ? gp.dk : gp.dv) +
                   (bh * a.n + pos) * D + col;
-  *dst = __builtin_bit_cast(uint16_t, (__bf16)(is_v ? s : s * a.scale));
+  *dst = __builtin_bit_cast(uint16_t, (__bf16)(which == 2 ? s : s * a.scale));
 }
 
 template <int D, int NW, int MODE>
 hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream_t s,
                         const LaunchEvents* ev) {
-  const long rows = (long)a.B * a.H * a.n;
   auto timed = [&](int i, auto kernel, dim3 gr, dim3 bl, auto... xs) {
     if (ev && (ev[i].start || ev[i].stop))
       hipExtLaunchKernelGGL(kernel, gr, bl, 0, s, ev[i].start, ev[i].stop, 0, xs...);
     else
       hipLaunchKernelGGL(kernel, gr, bl, 0, s, xs...);
   };
-  timed(0, bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), a, g, rows);
-  timed(1, attn_bwd_kernel<D, kBwdDQ, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), a, g);
-  const long grows = (long)a.B * a.H * a.g;
-  if (grows > 0) {
-    FwdArgs a2 = a;
-    hipLaunchKernelGGL((bwd_global_combine_kernel<D, kBwdDQ>), dim3((unsigned)grows),
-                       dim3(256), 0, s, a2, g);
-  }
+  timed(0, attn_bwd_kernel<D, kBwdDQ, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), a, g);
   // the dK/dV partials live after the dQ partials
   FwdArgs ak = a;
   ak.part = a.part + (size_t)a.B * a.H * a.g * a.chunks * D;
-  timed(2, attn_bwd_kernel<D, kBwdDKV, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), ak, g);
+  timed(1, attn_bwd_kernel<D, kBwdDKV, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), ak, g);
+  const long grows = (long)a.B * a.H * a.g;
   if (grows > 0)
-    hipLaunchKernelGGL((bwd_global_combine_kernel<D, kBwdDKV>), dim3((unsigned)grows),
-                       dim3(256), 0, s, ak, g);
+    timed(2, bwd_global_combine_kernel<D>, dim3((unsigned)grows), dim3(3 * D), a, g);
+  else if (ev && (hipEventRecord(ev[2].start, s) != hipSuccess ||
+                  hipEventRecord(ev[2].stop, s) != hipSuccess))
+    return hipErrorUnknown;
   return hipGetLastError();
 }
 
