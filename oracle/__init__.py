@@ -8,7 +8,8 @@ use is the seeded input generator package ``workloads``.
 The arithmetic lives in ``longattn_oracle.c`` (plain C, fp64, OpenMP); what it computes and
 which passage each step follows is written at the top of that file.  ``decode_inputs`` states a
 decode step over a key/value cache as that same forward pass on the gathered window;
-``backward`` gives the exact gradients of the forward pass.  Every function is pinned
+``backward`` gives the exact gradients of the forward pass; ``tglobal_side`` and
+``tglobal_forward`` state LongT5's Transient-Global attention.  Every function is pinned
 by the CPU tests (dense brute force, library full/causal attention, the Big Bird worked window
 example, closed-form counts and invariants); none is left "parity unpinned".
 """
@@ -58,6 +59,17 @@ def _bind(lib):
     lib.longattn_oracle_backward.argtypes = [
         _I64, _I64, _I64, _I64, ctypes.c_double, _I64, _I64, _P, _P, _I64, _P, _P,
         _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int,
+    ]
+    lib.longattn_oracle_t5_bucket.restype = ctypes.c_int64
+    lib.longattn_oracle_t5_bucket.argtypes = [_I64, _I64, _I64]
+    lib.longattn_oracle_tglobal_side.restype = ctypes.c_int
+    lib.longattn_oracle_tglobal_side.argtypes = [
+        _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_double, _P, _P, _P, _P, _P, _P, _P, _P,
+    ]
+    lib.longattn_oracle_tglobal_forward.restype = ctypes.c_int
+    lib.longattn_oracle_tglobal_forward.argtypes = [
+        _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_double, _P, _P, _P, _P, _P, _P,
+        _P, _P, _P, _P, _P, _P, ctypes.c_int,
     ]
     lib.longattn_oracle_row_set.restype = ctypes.c_int64
     lib.longattn_oracle_row_set.argtypes = [
@@ -251,3 +263,79 @@ def decode_inputs(inp, samples=None, nthreads: int = 0):
         outs.append(o[0, :, L - inp.m:])
         lses.append(l[0, :, L - inp.m:])
     return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------- Transient-Global attention
+def t5_bucket(rel: int, num_buckets: int = 32, max_distance: int = 128) -> int:
+    """T5 bidirectional relative-position bucket of key position - query position."""
+    return int(_load().longattn_oracle_t5_bucket(int(rel), int(num_buckets), int(max_distance)))
+
+
+def num_global(n: int, block: int) -> int:
+    """Global tokens of a sequence of n tokens with blocks of ``block`` (the tail merges)."""
+    return max(1, n // block)
+
+
+def tglobal_side(x: np.ndarray, gamma: np.ndarray, wk: np.ndarray, wv: np.ndarray, *,
+                 heads: int, d: int, block: int, eps: float, key_pad=None):
+    """Global tokens' keys and values.  x [B, n, dm]; gamma [dm]; wk, wv [dm, heads*d].
+    Returns (side_k, side_v [B, heads, G, d] fp64, side_valid [B, G] uint8)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    B, n, dm = x.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float64)
+    wk = np.ascontiguousarray(wk, dtype=np.float64)
+    wv = np.ascontiguousarray(wv, dtype=np.float64)
+    assert gamma.shape == (dm,) and wk.shape == (dm, heads * d) and wv.shape == wk.shape
+    G = num_global(n, block)
+    sk = np.empty((B, heads, G, d))
+    sv = np.empty((B, heads, G, d))
+    valid = np.empty((B, G), dtype=np.uint8)
+    kp = None if key_pad is None else np.ascontiguousarray(key_pad, dtype=np.uint8)
+    rc = _load().longattn_oracle_tglobal_side(B, n, dm, heads, d, block, float(eps), _ptr(x),
+                                              _ptr(gamma), _ptr(wk), _ptr(wv), _ptr(kp),
+                                              _ptr(sk), _ptr(sv), _ptr(valid))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return sk, sv, valid
+
+
+def tglobal_forward(q, k, v, side_k, side_v, side_valid, *, radius: int, block: int,
+                    num_buckets: int, max_distance: int, scale: float, bias_local, bias_side,
+                    key_pad=None, nthreads: int = 0):
+    """Transient-Global attention.  Returns (out [B,H,n,d], lse [B,H,n], E)."""
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v))
+    side_k = np.ascontiguousarray(side_k, dtype=np.float64)
+    side_v = np.ascontiguousarray(side_v, dtype=np.float64)
+    sval = np.ascontiguousarray(side_valid, dtype=np.uint8)
+    bl = np.ascontiguousarray(bias_local, dtype=np.float64)
+    bs = np.ascontiguousarray(bias_side, dtype=np.float64)
+    B, H, n, d = q.shape
+    G = num_global(n, block)
+    assert side_k.shape == (B, H, G, d) and side_v.shape == side_k.shape
+    assert sval.shape == (B, G) and bl.shape == (num_buckets, H) and bs.shape == bl.shape
+    kp = None if key_pad is None else np.ascontiguousarray(key_pad, dtype=np.uint8)
+    out = np.empty_like(q)
+    lse = np.empty((B, H, n))
+    E = ctypes.c_int64(0)
+    rc = _load().longattn_oracle_tglobal_forward(
+        B, H, n, d, int(radius), int(block), int(num_buckets), int(max_distance), float(scale),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(side_k), _ptr(side_v), _ptr(sval), _ptr(kp), _ptr(bl),
+        _ptr(bs), _ptr(out), _ptr(lse), ctypes.byref(E), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out, lse, int(E.value)
+
+
+def tglobal_inputs(inp, nthreads: int = 0):
+    """Both oracle steps on a ``workloads.tglobal.TGInputs``: (out, lse, E, side_k, side_v,
+    side_valid)."""
+    sk, sv, valid = tglobal_side(inp.f64("x"), inp.gamma, inp.f64("wk"), inp.f64("wv"),
+                                 heads=inp.heads, d=inp.d, block=inp.block, eps=inp.eps,
+                                 key_pad=inp.key_pad)
+    out, lse, E = tglobal_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), sk, sv, valid,
+                                  radius=inp.radius, block=inp.block,
+                                  num_buckets=inp.num_buckets, max_distance=inp.max_distance,
+                                  scale=inp.scale, bias_local=inp.bias_local,
+                                  bias_side=inp.bias_side, key_pad=inp.key_pad,
+                                  nthreads=nthreads)
+    return out, lse, E, sk, sv, valid

@@ -383,3 +383,186 @@ int longattn_oracle_backward(int64_t B, int64_t H, int64_t n, int64_t d, double 
   free(is_global);
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * LongT5 Transient-Global attention (LongT5 guide, sections on TGlobal attention, the block and
+ * side helpers, and relative position encoding).
+ *
+ * Global tokens.  The sequence is cut into fixed blocks of `blk` tokens (k = 16 by default); a
+ * token's block id is i / blk, except that the trailing incomplete block (if any) merges into
+ * the block before it, so there are G = max(1, n / blk) global tokens and block(i) =
+ * min(i / blk, G - 1); padded tokens belong to no block.  Global token g of sample b is the sum
+ * of the embeddings x of the non-padded tokens of block g, RMS-normalised (y = s / sqrt(mean(s^2)
+ * + eps) * gamma, the T5 layer norm), then projected with the attention's key and value
+ * weights: side_k[b, h, g] = y . Wk[:, h*d : (h+1)*d], side_v likewise.  A block without any
+ * non-padded token gives no global token (side_valid = 0).
+ *
+ * Attention.  Query i (head h) attends
+ *   the local keys j with |i - j| <= radius that are not padded, score scale * q_i . k_j +
+ *   bias_local[bucket(j - i)][h], and
+ *   every valid global token g, score scale * q_i . side_k[g] + bias_side[bucket(g - block(i))][h],
+ * all in one softmax (the side keys join the local keys); out = sum of weights times the local
+ * values and the side values; lse as in the forward pass.  E counts the (query, key) pairs:
+ * O(n (r + n/k)) (the guide's cost law).
+ *
+ * Relative position buckets (T5's bidirectional scheme, as the guide describes it): half of the
+ * buckets are for positive distances (key after query), half for the rest; within a half,
+ * distances below half/2 get one bucket each, larger ones share log-spaced buckets up to
+ * max_distance, and everything farther falls in the half's last bucket:
+ *   h = nb / 2; base = (rel > 0) ? h : 0; a = |rel|; e = h / 2;
+ *   a < e:  base + a;  else base + min(h - 1, e + floor(log(a / e) / log(md / e) * (h - e))).
+ * fp64 throughout.
+ * ------------------------------------------------------------------------------------------ */
+int64_t longattn_oracle_t5_bucket(int64_t rel, int64_t num_buckets, int64_t max_distance) {
+  const int64_t half = num_buckets / 2;
+  const int64_t base = rel > 0 ? half : 0;
+  const int64_t a = rel < 0 ? -rel : rel;
+  const int64_t exact = half / 2;
+  if (a < exact) return base + a;
+  const double x = log((double)a / (double)exact) / log((double)max_distance / (double)exact) *
+                   (double)(half - exact);
+  int64_t off = exact + (int64_t)floor(x);
+  if (off > half - 1) off = half - 1;
+  return base + off;
+}
+
+static int64_t tg_num_global(int64_t n, int64_t blk) {
+  int64_t G = n / blk;
+  return G < 1 ? 1 : G;
+}
+
+/* Global tokens.  x: [B][n][dm]; gamma: [dm]; wk, wv: [dm][H*d]; key_pad: [B][n] or NULL.
+ * side_k, side_v: [B][H][G][d]; side_valid: [B][G] (1 = the block has a non-padded token). */
+int longattn_oracle_tglobal_side(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d,
+                                 int64_t blk, double eps, const double* x, const double* gamma,
+                                 const double* wk, const double* wv, const uint8_t* key_pad,
+                                 double* side_k, double* side_v, uint8_t* side_valid) {
+  if (B < 0 || n < 1 || dm < 1 || H < 1 || d < 1 || blk < 1 || !(eps >= 0.0)) return ORACLE_BAD_ARG;
+  if (!x || !gamma || !wk || !wv || !side_k || !side_v || !side_valid) return ORACLE_BAD_ARG;
+  const int64_t G = tg_num_global(n, blk);
+  double* s = (double*)malloc((size_t)dm * sizeof(double));
+  double* y = (double*)malloc((size_t)dm * sizeof(double));
+  if (!s || !y) {
+    free(s);
+    free(y);
+    return ORACLE_NO_MEMORY;
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t g = 0; g < G; ++g) {
+      /* sum of the block's non-padded token embeddings (the merged tail included) */
+      for (int64_t c = 0; c < dm; ++c) s[c] = 0.0;
+      int any = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        int64_t bi = i / blk;
+        if (bi > G - 1) bi = G - 1;
+        if (bi != g) continue;
+        if (key_pad && key_pad[b * n + i]) continue;
+        any = 1;
+        for (int64_t c = 0; c < dm; ++c) s[c] += x[(b * n + i) * dm + c];
+      }
+      side_valid[b * G + g] = (uint8_t)any;
+      /* RMS normalisation */
+      double ms = 0.0;
+      for (int64_t c = 0; c < dm; ++c) ms += s[c] * s[c];
+      ms /= (double)dm;
+      const double inv = 1.0 / sqrt(ms + eps);
+      for (int64_t c = 0; c < dm; ++c) y[c] = s[c] * inv * gamma[c];
+      /* projections */
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t c = 0; c < d; ++c) {
+          double ak = 0.0, av = 0.0;
+          for (int64_t m = 0; m < dm; ++m) {
+            ak += y[m] * wk[m * (H * d) + h * d + c];
+            av += y[m] * wv[m * (H * d) + h * d + c];
+          }
+          side_k[((b * H + h) * G + g) * d + c] = ak;
+          side_v[((b * H + h) * G + g) * d + c] = av;
+        }
+    }
+  }
+  free(s);
+  free(y);
+  return ORACLE_OK;
+}
+
+/* Attention.  q, k, v, out: [B][H][n][d]; side_k, side_v: [B][H][G][d]; side_valid: [B][G];
+ * key_pad: [B][n] or NULL; bias_local, bias_side: [num_buckets][H]; lse: [B][H][n] or NULL. */
+int longattn_oracle_tglobal_forward(int64_t B, int64_t H, int64_t n, int64_t d, int64_t radius,
+                                    int64_t blk, int64_t num_buckets, int64_t max_distance,
+                                    double scale, const double* q, const double* k,
+                                    const double* v, const double* side_k, const double* side_v,
+                                    const uint8_t* side_valid, const uint8_t* key_pad,
+                                    const double* bias_local, const double* bias_side,
+                                    double* out, double* lse, int64_t* E_out, int nthreads) {
+  if (B < 0 || H < 1 || n < 1 || d < 1 || radius < 0 || blk < 1 || num_buckets < 4 ||
+      max_distance < 1)
+    return ORACLE_BAD_ARG;
+  if (!q || !k || !v || !side_k || !side_v || !side_valid || !bias_local || !bias_side || !out)
+    return ORACLE_BAD_ARG;
+  const int64_t G = tg_num_global(n, blk);
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  int64_t E = 0;
+  int failed = 0;
+  const int64_t rows = B * H * n;
+#pragma omp parallel num_threads(nthreads) reduction(+ : E) reduction(| : failed)
+  {
+    const size_t cap = (size_t)(2 * radius + 1 + G);
+    double* sc = (double*)malloc(cap * sizeof(double));
+    const double** vr = (const double**)malloc(cap * sizeof(double*));
+    if (!sc || !vr) failed = 1;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (failed) continue;
+      const int64_t i = r % n, bh = r / n, h = bh % H, b = bh / H;
+      const double* qi = q + r * d;
+      int64_t cnt = 0;
+      /* local keys */
+      const int64_t j0 = i - radius < 0 ? 0 : i - radius;
+      const int64_t j1 = i + radius > n - 1 ? n - 1 : i + radius;
+      for (int64_t j = j0; j <= j1; ++j) {
+        if (key_pad && key_pad[b * n + j]) continue;
+        const double* kj = k + (bh * n + j) * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        sc[cnt] = scale * dot + bias_local[longattn_oracle_t5_bucket(j - i, num_buckets, max_distance) * H + h];
+        vr[cnt] = v + (bh * n + j) * d;
+        ++cnt;
+      }
+      /* global tokens */
+      int64_t bi = i / blk;
+      if (bi > G - 1) bi = G - 1;
+      for (int64_t g = 0; g < G; ++g) {
+        if (!side_valid[b * G + g]) continue;
+        const double* kg = side_k + (bh * G + g) * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kg[c];
+        sc[cnt] = scale * dot + bias_side[longattn_oracle_t5_bucket(g - bi, num_buckets, max_distance) * H + h];
+        vr[cnt] = side_v + (bh * G + g) * d;
+        ++cnt;
+      }
+      E += cnt;
+      double* oi = out + r * d;
+      for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+      if (cnt == 0) {
+        if (lse) lse[r] = -INFINITY;
+        continue;
+      }
+      double m = -INFINITY;
+      for (int64_t t = 0; t < cnt; ++t)
+        if (sc[t] > m) m = sc[t];
+      double l = 0.0;
+      for (int64_t t = 0; t < cnt; ++t) {
+        const double w = exp(sc[t] - m);
+        l += w;
+        for (int64_t c = 0; c < d; ++c) oi[c] += w * vr[t][c];
+      }
+      for (int64_t c = 0; c < d; ++c) oi[c] /= l;
+      if (lse) lse[r] = m + log(l);
+    }
+    free(sc);
+    free(vr);
+  }
+  if (failed) return ORACLE_NO_MEMORY;
+  if (E_out) *E_out = E;
+  return ORACLE_OK;
+}

@@ -91,6 +91,37 @@ BWD_PINS = [
 ]
 
 
+# Planted mistakes in the Transient-Global attention, caught by its pins.
+from tests import test_oracle_tglobal as tpins  # noqa: E402
+
+TG_MUTANTS = {
+    "tg_side_bias_sign": ("longattn_oracle_t5_bucket(g - bi, num_buckets, max_distance)",
+                          "longattn_oracle_t5_bucket(bi - g, num_buckets, max_distance)"),
+    "tg_rms_without_sqrt": ("const double inv = 1.0 / sqrt(ms + eps);",
+                            "const double inv = 1.0 / (ms + eps);"),
+    "tg_window_short_on_the_right": ("const int64_t j1 = i + radius > n - 1 ? n - 1 : i + radius;",
+                                     "const int64_t j1 = i + radius > n - 1 ? n - 1 : i + radius - 1;"),
+    "tg_side_padding_ignored": ("if (key_pad && key_pad[b * n + i]) continue;", ""),
+    "tg_log_ratio_swapped": ("const double x = log((double)a / (double)exact) / log((double)max_distance / (double)exact) *",
+                             "const double x = log((double)max_distance / (double)exact) / log((double)a / (double)exact) *"),
+    "tg_positive_half_swapped": ("const int64_t base = rel > 0 ? half : 0;",
+                                 "const int64_t base = rel < 0 ? half : 0;"),
+}
+
+TG_PINS = [
+    lambda: [tpins.test_bucket_matches_integer_statement(nb, md)
+             for nb, md in [(32, 128), (16, 64)]],
+    tpins.test_bucket_shape_of_the_rule,
+    lambda: [tpins.test_side_tokens_match_brute_force(n, b)
+             for n, b in [(70, 8), (64, 16), (5, 16), (33, 16)]],
+    tpins.test_rms_norm_gives_unit_rms_and_the_tail_block_merges,
+    lambda: [tpins.test_forward_matches_dense_brute_force(kw)
+             for kw in [dict(), dict(radius=0), dict(pad_tail=(5, 40))]],
+    tpins.test_without_bias_and_with_a_full_window_it_is_attention_over_concatenated_keys,
+    lambda: tpins.test_entry_count_closed_form(300, 5, 8),
+]
+
+
 def _caught(lib_path, pins_list=None):
     failures = 0
     with oracle.substituted_library(lib_path):
@@ -128,9 +159,23 @@ def test_planted_backward_mistake_is_caught(name, tmp_path):
     assert _caught(str(so), BWD_PINS) >= 1, f"no pin catches the planted mistake {name}"
 
 
+@pytest.mark.parametrize("name", sorted(TG_MUTANTS))
+def test_planted_tglobal_mistake_is_caught(name, tmp_path):
+    old, new = TG_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(mutant_c), "-lm"], check=True, capture_output=True)
+    assert _caught(str(so), TG_PINS) >= 1, f"no pin catches the planted mistake {name}"
+
+
 def test_unmutated_copy_passes_every_pin(tmp_path):
     so = tmp_path / "libcopy.so"
     subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
                     SRC, "-lm"], check=True, capture_output=True)
     assert _caught(str(so)) == 0
     assert _caught(str(so), BWD_PINS) == 0
+    assert _caught(str(so), TG_PINS) == 0
