@@ -544,7 +544,7 @@ int longattn_oracle_tglobal_forward(int64_t B, int64_t H, int64_t n, int64_t d, 
       double* oi = out + r * d;
       for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
       if (cnt == 0) {
-        if (lse) lse[r] = -INFINITY;
+        if (lse != NULL) lse[r] = -INFINITY;
         continue;
       }
       double m = -INFINITY;
@@ -557,7 +557,7 @@ int longattn_oracle_tglobal_forward(int64_t B, int64_t H, int64_t n, int64_t d, 
         for (int64_t c = 0; c < d; ++c) oi[c] += w * vr[t][c];
       }
       for (int64_t c = 0; c < d; ++c) oi[c] /= l;
-      if (lse) lse[r] = m + log(l);
+      if (lse != NULL) lse[r] = m + log(l);
     }
     free(sc);
     free(vr);
