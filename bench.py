@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --decode swa512_decode_32k [--steps K] [--warmup W]
     python bench.py --backward [--workload NAME] [--steps K] [--warmup W]
+    python bench.py --tglobal tglobal_16k [--steps K] [--warmup W]
 
 One step is one full forward pass (global-row partials, main sparse kernel, global-row combine)
 over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
@@ -44,6 +45,9 @@ def _parse():
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward bench: time the backward pass (dQ, dK, dV from "
                          "the saved out and lse) of the workload")
+    ap.add_argument("--tglobal", default=None, metavar="NAME",
+                    help="instead of the forward bench: time LongT5 Transient-Global attention "
+                         "(global-token pass + attention) on the named workload (tglobal_16k)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the attention bench: time K device-to-device copies of this "
                          "many MiB (a kernel of known HBM traffic, used to calibrate the "
@@ -279,6 +283,135 @@ def _backward_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _tglobal_bench(args):
+    """Transient-Global steps: the global-token pass (block sums, RMS norm, key and value
+    projections) and the attention (local window plus every global token, bucketed biases).
+    Useful work: 4*d per attended (query, key) pair plus 2*d_model*H*d per global token and
+    projection."""
+    import numpy as np
+    import torch
+
+    import sparse_long_sequence_banded_amd as la
+    from workloads.tglobal import TG_WORKLOADS, tglobal_to_torch, tglobal_workload_inputs
+
+    wl = TG_WORKLOADS[args.tglobal]
+    inp = tglobal_workload_inputs(wl)
+    t = tglobal_to_torch(inp, "cuda:0")
+    B, H, n, d = inp.batch, inp.heads, inp.n, inp.d
+    G = max(1, n // inp.block)
+    desc = la.make_tglobal_desc(t["q"], d_model=inp.d_model, radius=inp.radius, block=inp.block,
+                                scale=inp.scale, num_buckets=inp.num_buckets,
+                                max_distance=inp.max_distance, eps=inp.eps, key_pad=t["key_pad"])
+    _, wsb = la.longattn_tglobal_workspace_size(desc)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda:0")
+    sk = torch.empty((B, H, G, d), dtype=torch.bfloat16, device="cuda:0")
+    sv = torch.empty_like(sk)
+    valid = torch.empty((B, G), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, n), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def side():
+        st = la.longattn_tglobal_side(desc, t["x"].data_ptr(), t["gamma"].data_ptr(),
+                                      t["wk"].data_ptr(), t["wv"].data_ptr(), sk.data_ptr(),
+                                      sv.data_ptr(), valid.data_ptr(), ws.data_ptr(), wsb, sh)
+        if st != la.LONGATTN_OK:
+            raise la.LongAttnError(st, "longattn_tglobal_side")
+
+    def attn():
+        st = la.longattn_tglobal_forward(desc, t["q"].data_ptr(), t["k"].data_ptr(),
+                                         t["v"].data_ptr(), sk.data_ptr(), sv.data_ptr(),
+                                         valid.data_ptr(), t["bias_local"].data_ptr(),
+                                         t["bias_side"].data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), ws.data_ptr(), wsb, sh)
+        if st != la.LONGATTN_OK:
+            raise la.LongAttnError(st, "longattn_tglobal_forward")
+
+    for _ in range(args.warmup):
+        side()
+        attn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        side()
+        attn()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        side()
+        ev[s_][1].record(stream)
+        attn()
+        ev[s_][2].record(stream)
+    torch.cuda.synchronize()
+    side_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    if inp.key_pad is None:
+        r = min(inp.radius, n - 1)
+        E = B * H * (n * (2 * r + 1) - r * (r + 1) + n * G)
+    else:
+        raise SystemExit("padded Transient-Global workloads are parity cases, not bench lines")
+    side_flop = 2.0 * 2 * B * G * inp.d_model * H * d
+    useful = 4.0 * d * E + side_flop
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    attn_tf = 4.0 * d * E / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "useful TFLOP/s of LongT5 Transient-Global attention (global-token pass + "
+                  "attention, 1 GPU)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "seq_len": n, "head_dim": d,
+                   "d_model": inp.d_model, "radius": inp.radius, "global_block": inp.block,
+                   "global_tokens": G, "useful_entries": E, "description": wl.note},
+        "kernels_ms": {"global_tokens": round(side_ms, 5), "attention": round(attn_ms, 5)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "tg_attn_kernel (events around the attention call: bias vectors + kernel)",
+            "achieved": round(attn_tf, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        hs = [0]
+        t0 = time.perf_counter()
+        sk64, sv64, val64 = oracle.tglobal_side(inp.f64("x"), inp.gamma, inp.f64("wk"),
+                                                inp.f64("wv"), heads=H, d=d, block=inp.block,
+                                                eps=inp.eps)
+        oracle.tglobal_forward(inp.f64("q")[:, hs], inp.f64("k")[:, hs], inp.f64("v")[:, hs],
+                               sk64[:, hs], sv64[:, hs], val64, radius=inp.radius,
+                               block=inp.block, num_buckets=inp.num_buckets,
+                               max_distance=inp.max_distance, scale=inp.scale,
+                               bias_local=inp.bias_local[:, hs], bias_side=inp.bias_side[:, hs],
+                               nthreads=threads)
+        dt = time.perf_counter() - t0
+        work = side_flop + 4.0 * d * E / H
+        rec["cpu_baseline"] = {
+            "value": round(work / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the global-token pass of all {H} heads + attention of head 0, "
+                      f"{work / 1e9:.1f} GFLOP fp64, {dt:.2f} s"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def _source_hash():
     with open(MAIN_KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -343,6 +476,9 @@ def main():
         return
     if args.backward:
         _backward_bench(args)
+        return
+    if args.tglobal:
+        _tglobal_bench(args)
         return
 
     import numpy as np

@@ -155,6 +155,58 @@ longattn_status longattn_backward_marked(const longattn_desc* desc, const void* 
                                          void* stream, void* const* marks, int32_t n_marks);
 
 /* ---------------------------------------------------------------------------------------
+ * LongT5 Transient-Global attention (LongT5 guide: Transient-Global attention, the block and
+ * side helpers, relative position encoding).
+ *
+ * Global tokens: the sequence is cut into blocks of `block` tokens (k = 16 by default); the
+ * trailing incomplete block merges into the one before it, so there are G = max(1, n / block)
+ * global tokens and token i belongs to block min(i / block, G - 1).  Global token g of sample b
+ * is the sum of the embeddings x of the block's non-padded tokens, RMS-normalised
+ * (y = s / sqrt(mean(s^2) + eps) * gamma) and projected with the attention's key and value
+ * weights: side_k[b][h][g] = y . wk[:, h*d : (h+1)*d], side_v likewise.  side_valid[b][g] = 0
+ * when the block has no non-padded token.
+ *
+ * Attention: query i of head h attends the local keys j with |i - j| <= radius (not padded),
+ * score scale * q_i . k_j + bias_local[bucket(j - i)][h], and every valid global token g, score
+ * scale * q_i . side_k[g] + bias_side[bucket(g - block(i))][h], all in one softmax; out and lse
+ * as in longattn_forward.  bucket() is T5's bidirectional relative-position bucket with
+ * num_buckets buckets and max_distance (half the buckets per direction, exact below a quarter
+ * of num_buckets, log-spaced up to max_distance, saturated beyond).
+ *
+ * Tensors (DEVICE): x [B][n][d_model] bf16; gamma fp32 [d_model]; wk, wv bf16 [d_model][H*d];
+ * q, k, v, out bf16 [B][H][n][d]; side_k, side_v bf16 [B][H][G][d] (written by
+ * longattn_tglobal_side, read by longattn_tglobal_forward); side_valid uint8 [B][G]; bias
+ * tables fp32 [num_buckets][H]; lse fp32 [B][H][n] or NULL.  Kernels: bf16, d in {64, 128},
+ * radius <= 512, max_distance <= 512, num_buckets even in [4, 256], d_model a multiple of 64
+ * and <= 4096 (the normalised global inputs are rounded to bf16 before the projections); other
+ * valid values return LONGATTN_ERR_UNSUPPORTED.  Workspace: longattn_tglobal_workspace_size
+ * bytes (covers both calls).
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch, heads, n, d;
+  int32_t d_model;
+  float scale;                 /* > 0 and finite                                                 */
+  int32_t radius;              /* local radius r >= 0                                            */
+  int32_t block;               /* global block length k >= 1                                     */
+  int32_t num_buckets;         /* even, >= 4                                                     */
+  int32_t max_distance;        /* >= 1                                                           */
+  float eps;                   /* RMS-norm epsilon, >= 0                                         */
+  const uint8_t* key_pad;      /* DEVICE [batch][n], nonzero = padded token; NULL = none         */
+} longattn_tglobal_desc;
+
+longattn_status longattn_tglobal_workspace_size(const longattn_tglobal_desc* desc, size_t* bytes);
+longattn_status longattn_tglobal_side(const longattn_tglobal_desc* desc, const void* x,
+                                      const float* gamma, const void* wk, const void* wv,
+                                      void* side_k, void* side_v, uint8_t* side_valid,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+longattn_status longattn_tglobal_forward(const longattn_tglobal_desc* desc, const void* q,
+                                         const void* k, const void* v, const void* side_k,
+                                         const void* side_v, const uint8_t* side_valid,
+                                         const float* bias_local, const float* bias_side,
+                                         void* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Sliding-window decode over a key/value cache.
  *
  * The incremental form of the causal sliding window used by the SWA decoder layers (SWAN-GPT

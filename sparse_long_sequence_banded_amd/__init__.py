@@ -39,6 +39,9 @@ EXPORTED = (
     "longattn_backward_workspace_size",
     "longattn_backward",
     "longattn_backward_marked",
+    "longattn_tglobal_workspace_size",
+    "longattn_tglobal_side",
+    "longattn_tglobal_forward",
     "longattn_decode_workspace_size",
     "longattn_decode",
     "longattn_status_string",
@@ -81,6 +84,25 @@ class longattn_decode_desc(ctypes.Structure):
         ("cache_len", ctypes.c_int32),
         ("ring", ctypes.c_int32),
         ("positions", ctypes.c_void_p),
+    ]
+
+
+class longattn_tglobal_desc(ctypes.Structure):
+    """Mirror of ``longattn_tglobal_desc`` in include/longattn.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("radius", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("num_buckets", ctypes.c_int32),
+        ("max_distance", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("key_pad", ctypes.c_void_p),
     ]
 
 
@@ -128,6 +150,14 @@ def load():
                                                      ctypes.POINTER(ctypes.c_void_p),
                                                      ctypes.c_int32]
             lib.longattn_backward_marked.restype = ctypes.c_int
+            TD = ctypes.POINTER(longattn_tglobal_desc)
+            lib.longattn_tglobal_workspace_size.argtypes = [TD, ctypes.POINTER(ctypes.c_size_t)]
+            lib.longattn_tglobal_workspace_size.restype = ctypes.c_int
+            lib.longattn_tglobal_side.argtypes = [TD, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.longattn_tglobal_side.restype = ctypes.c_int
+            lib.longattn_tglobal_forward.argtypes = [TD, P, P, P, P, P, P, P, P, P, P, P,
+                                                     ctypes.c_size_t, P]
+            lib.longattn_tglobal_forward.restype = ctypes.c_int
             DD = ctypes.POINTER(longattn_decode_desc)
             lib.longattn_decode_workspace_size.argtypes = [DD, ctypes.POINTER(ctypes.c_size_t)]
             lib.longattn_decode_workspace_size.restype = ctypes.c_int
@@ -445,3 +475,78 @@ def decode(q, k_cache, v_cache, positions, *, window: int, scale: Optional[float
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_decode")
     return out, lse
+
+
+# ---------------------------------------------------------------------- Transient-Global attention
+def longattn_tglobal_workspace_size(desc: longattn_tglobal_desc) -> Tuple[int, int]:
+    nbytes = ctypes.c_size_t(0)
+    st = load().longattn_tglobal_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes))
+    return st, int(nbytes.value)
+
+
+def longattn_tglobal_side(desc, x, gamma, wk, wv, side_k, side_v, side_valid, workspace,
+                          workspace_bytes, stream) -> int:
+    return load().longattn_tglobal_side(ctypes.byref(desc), x, gamma, wk, wv, side_k, side_v,
+                                        side_valid, workspace, int(workspace_bytes), stream)
+
+
+def longattn_tglobal_forward(desc, q, k, v, side_k, side_v, side_valid, bias_local, bias_side,
+                             out, lse, workspace, workspace_bytes, stream) -> int:
+    return load().longattn_tglobal_forward(ctypes.byref(desc), q, k, v, side_k, side_v,
+                                           side_valid, bias_local, bias_side, out, lse,
+                                           workspace, int(workspace_bytes), stream)
+
+
+def make_tglobal_desc(q, *, d_model: int, radius: int, block: int, scale: Optional[float] = None,
+                      num_buckets: int = 32, max_distance: int = 128, eps: float = 1e-6,
+                      key_pad=None) -> longattn_tglobal_desc:
+    B, H, n, d = q.shape
+    return longattn_tglobal_desc(
+        batch=B, heads=H, n=n, d=d, d_model=int(d_model),
+        scale=float(scale) if scale is not None else 1.0 / float(d) ** 0.5,
+        radius=int(radius), block=int(block), num_buckets=int(num_buckets),
+        max_distance=int(max_distance), eps=float(eps),
+        key_pad=None if key_pad is None else key_pad.data_ptr())
+
+
+def tglobal(x, gamma, wk, wv, q, k, v, bias_local, bias_side, *, radius: int = 127,
+            block: int = 16, scale: Optional[float] = None, num_buckets: int = 32,
+            max_distance: int = 128, eps: float = 1e-6, key_pad=None, want_lse: bool = True,
+            stream=None):
+    """LongT5 Transient-Global attention on device tensors: x [B, n, d_model] bf16, gamma fp32,
+    wk, wv [d_model, H*d] bf16, q, k, v [B, H, n, d] bf16, bias tables fp32 [num_buckets, H].
+    Returns (out, lse, side_k, side_v, side_valid)."""
+    import torch
+
+    B, H, n, d = q.shape
+    for t in (x, wk, wv, q, k, v, gamma, bias_local, bias_side):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("every tensor must be a contiguous device tensor")
+    if key_pad is not None and (key_pad.dtype != torch.uint8 or key_pad.shape != (B, n)):
+        raise ValueError("key_pad must be uint8 [B, n]")
+    desc = make_tglobal_desc(q, d_model=x.shape[-1], radius=radius, block=block, scale=scale,
+                             num_buckets=num_buckets, max_distance=max_distance, eps=eps,
+                             key_pad=key_pad)
+    st, ws_bytes = longattn_tglobal_workspace_size(desc)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_tglobal_workspace_size")
+    G = max(1, n // block)
+    side_k = torch.empty((B, H, G, d), dtype=q.dtype, device=q.device)
+    side_v = torch.empty_like(side_k)
+    side_valid = torch.empty((B, G), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    sh = _stream_handle(stream)
+    st = longattn_tglobal_side(desc, x.data_ptr(), gamma.data_ptr(), wk.data_ptr(),
+                               wv.data_ptr(), side_k.data_ptr(), side_v.data_ptr(),
+                               side_valid.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_tglobal_side")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if want_lse else None
+    st = longattn_tglobal_forward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  side_k.data_ptr(), side_v.data_ptr(), side_valid.data_ptr(),
+                                  bias_local.data_ptr(), bias_side.data_ptr(), out.data_ptr(),
+                                  _ptr(lse), ws.data_ptr(), ws_bytes, sh)
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_tglobal_forward")
+    return out, lse, side_k, side_v, side_valid

@@ -85,6 +85,29 @@ struct DecodeConfig {
 };
 DecodeConfig decode_config(bool bf16, int d, long span, long bh);
 
+// LongT5 Transient-Global attention.
+constexpr int kTgMaxRadius = 512;               // local radius limit of the kernels
+constexpr int kTgMaxRl = kTgMaxRadius + 191;    // local relative positions a workgroup meets
+constexpr int kTgMaxMd = 512;                   // max_distance limit
+constexpr int kTgMaxDm = 4096;                  // d_model limit (a multiple of 64)
+
+struct TgArgs {
+  const uint16_t* q;      // [B][H][n][D]
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* sk;     // [B][H][G][D] global tokens' keys and values
+  const uint16_t* sv;
+  uint8_t* side_valid;    // [B][G]
+  const uint8_t* kpad;    // [B][n] or null
+  float* bias;            // [H][2rl+1 + 2md+1] per-head bias vectors (log2 units)
+  uint16_t* out;          // [B][H][n][D]
+  float* lse;             // [B][H][n] or null
+  uint16_t* sk_out;       // side pass outputs
+  uint16_t* sv_out;
+  int B, H, n, D, dm, G, blk, radius, rl, md, nb;
+  float scale_log2, eps;
+};
+
 // Launchers (defined next to their kernels).
 int main_rows_per_workgroup(int mode, int d, int block);
 // Optional events that record a kernel's own start and end (attached to its dispatch).
@@ -105,5 +128,10 @@ hipError_t launch_bwd_rowwise(const FwdArgs& a, const BwdArgs& g, int d, bool bf
 hipError_t launch_bwd_mfma(const FwdArgs& a, const BwdArgs& g, int d, int mode, long grid,
                            hipStream_t s, const LaunchEvents* ev);
 constexpr int kBwdMaxLayoutBlocks = 1024;  // matrix-core backward: n / block limit
+hipError_t launch_tglobal_side(const TgArgs& a, const uint16_t* x, const float* gamma,
+                               const uint16_t* wk, const uint16_t* wv, uint16_t* y,
+                               hipStream_t s);
+hipError_t launch_tglobal_attention(const TgArgs& a, const float* tab_local,
+                                    const float* tab_side, hipStream_t s);
 
 }  // namespace longattn

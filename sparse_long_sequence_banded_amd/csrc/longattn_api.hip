@@ -242,6 +242,62 @@ longattn_status plan_backward(const longattn_desc* d, BwdPlan* B) {
 
 }  // namespace
 
+// ------------------------------------------------------------------------------ TGlobal
+namespace {
+
+struct TgPlan {
+  TgArgs a;
+  size_t y_floats = 0;     // side pass: normalised aggregates [B][G][d_model] (bf16; counted
+                           // here in floats, so half of it is slack)
+  size_t bias_floats = 0;  // attention: per-head bias vectors
+  size_t ws_bytes = 0;
+  bool empty = false;
+};
+
+longattn_status plan_tglobal(const longattn_tglobal_desc* d, TgPlan* P) {
+  if (!d) return LONGATTN_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->heads < 1 || d->n < 0 || d->d < 1 || d->d_model < 1)
+    return LONGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return LONGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(d->eps) || d->eps < 0.f) return LONGATTN_ERR_INVALID_ARG;
+  if (d->radius < 0 || d->block < 1 || d->num_buckets < 4 || d->num_buckets % 2 != 0 ||
+      d->max_distance < 1)
+    return LONGATTN_ERR_INVALID_ARG;
+  if (d->d != 64 && d->d != 128) return LONGATTN_ERR_UNSUPPORTED;
+  if (d->radius > kTgMaxRadius || d->max_distance > kTgMaxMd || d->num_buckets > 256 ||
+      d->d_model > kTgMaxDm || d->d_model % 64 != 0)
+    return LONGATTN_ERR_UNSUPPORTED;
+  if ((long)d->n * d->d * 2 > 0x7fffffffL || (long)d->heads * d->d > 0x7fffffffL / 2)
+    return LONGATTN_ERR_UNSUPPORTED;
+  const long tiles = ((long)d->n + 127) / 128;
+  if ((long)d->batch * d->heads * tiles > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  TgPlan& p = *P;
+  p = TgPlan();
+  TgArgs& a = p.a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = d->batch;
+  a.H = d->heads;
+  a.n = d->n;
+  a.D = d->d;
+  a.dm = d->d_model;
+  a.blk = d->block;
+  a.G = std::max(1, d->n / d->block);
+  a.radius = std::min(d->radius, std::max(d->n - 1, 0));
+  a.rl = a.radius + 191;
+  a.md = d->max_distance;
+  a.nb = d->num_buckets;
+  a.scale_log2 = d->scale * 1.44269504088896340736f;
+  a.eps = d->eps;
+  a.kpad = d->key_pad;
+  p.empty = a.B == 0 || a.n == 0;
+  p.y_floats = (size_t)a.B * a.G * a.dm;
+  p.bias_floats = (size_t)a.H * (2 * a.rl + 1 + 2 * a.md + 1);
+  p.ws_bytes = p.empty ? 0 : std::max(p.y_floats, p.bias_floats) * sizeof(float);
+  return LONGATTN_OK;
+}
+
+}  // namespace
+
 // ------------------------------------------------------------------------------ decode
 namespace {
 
@@ -476,6 +532,71 @@ longattn_status longattn_backward(const longattn_desc* desc, const void* q, cons
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return longattn_backward_marked(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace,
                                   workspace_bytes, stream, nullptr, 0);
+}
+
+longattn_status longattn_tglobal_workspace_size(const longattn_tglobal_desc* desc, size_t* bytes) {
+  if (!bytes) return LONGATTN_ERR_INVALID_ARG;
+  TgPlan p;
+  const longattn_status st = plan_tglobal(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  *bytes = p.ws_bytes;
+  return LONGATTN_OK;
+}
+
+longattn_status longattn_tglobal_side(const longattn_tglobal_desc* desc, const void* x,
+                                      const float* gamma, const void* wk, const void* wv,
+                                      void* side_k, void* side_v, uint8_t* side_valid,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  TgPlan p;
+  const longattn_status st = plan_tglobal(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  if (p.empty) return LONGATTN_OK;
+  if (!x || !gamma || !wk || !wv || !side_k || !side_v || !side_valid)
+    return LONGATTN_ERR_INVALID_ARG;
+  for (const void* t : {x, wk, wv, static_cast<const void*>(side_k),
+                        static_cast<const void*>(side_v)})
+    if (!aligned16(t)) return LONGATTN_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LONGATTN_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
+  TgArgs& a = p.a;
+  a.side_valid = side_valid;
+  a.sk_out = static_cast<uint16_t*>(side_k);
+  a.sv_out = static_cast<uint16_t*>(side_v);
+  const hipError_t e = launch_tglobal_side(
+      a, static_cast<const uint16_t*>(x), gamma, static_cast<const uint16_t*>(wk),
+      static_cast<const uint16_t*>(wv), static_cast<uint16_t*>(workspace),
+      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
+}
+
+longattn_status longattn_tglobal_forward(const longattn_tglobal_desc* desc, const void* q,
+                                         const void* k, const void* v, const void* side_k,
+                                         const void* side_v, const uint8_t* side_valid,
+                                         const float* bias_local, const float* bias_side,
+                                         void* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  TgPlan p;
+  const longattn_status st = plan_tglobal(desc, &p);
+  if (st != LONGATTN_OK) return st;
+  if (p.empty) return LONGATTN_OK;
+  if (!q || !k || !v || !side_k || !side_v || !side_valid || !bias_local || !bias_side || !out)
+    return LONGATTN_ERR_INVALID_ARG;
+  for (const void* t : {q, k, v, side_k, side_v, static_cast<const void*>(out)})
+    if (!aligned16(t)) return LONGATTN_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
+  TgArgs& a = p.a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sk = static_cast<const uint16_t*>(side_k);
+  a.sv = static_cast<const uint16_t*>(side_v);
+  a.side_valid = const_cast<uint8_t*>(side_valid);  // read only by the attention kernel
+  a.bias = static_cast<float*>(workspace);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  const hipError_t e = launch_tglobal_attention(a, bias_local, bias_side,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
 }
 
 longattn_status longattn_decode_workspace_size(const longattn_decode_desc* desc, size_t* bytes) {

@@ -292,3 +292,64 @@ def test_backward_matrix_core_workspace_formula():
     assert la.longattn_backward_workspace_size(_desc(d=96)) == (la.LONGATTN_OK, 2 * 256 * 4)
     assert la.longattn_backward_marked(_desc(), *([FAKE] * 9), FAKE, 1 << 30, None,
                                        [FAKE] * 3) == la.LONGATTN_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------------------ TGlobal
+def test_tglobal_descriptor_layout_matches_the_header(tmp_path):
+    fields = [f for f, _ in la.longattn_tglobal_desc._fields_]
+    src = tmp_path / "tlayout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "longattn.h"\nint main(void){\n'
+        + 'printf("%zu\\n", sizeof(longattn_tglobal_desc));\n'
+        + "".join(f'printf("%zu\\n", offsetof(longattn_tglobal_desc, {f}));\n' for f in fields)
+        + "return 0;}\n")
+    exe = tmp_path / "tlayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(la.longattn_tglobal_desc)
+    assert vals[1:] == [getattr(la.longattn_tglobal_desc, f).offset for f in fields]
+
+
+def _tdesc(**kw):
+    base = dict(batch=1, heads=8, n=16384, d=64, d_model=512, scale=0.125, radius=127, block=16,
+                num_buckets=32, max_distance=128, eps=1e-6, key_pad=None)
+    base.update(kw)
+    return la.longattn_tglobal_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(eps=-1.0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(radius=-1), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(block=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(num_buckets=31), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(num_buckets=2), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(d=96), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(radius=513), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(max_distance=600), la.LONGATTN_ERR_UNSUPPORTED),
+])
+def test_bad_tglobal_descriptors_are_rejected(kw, status):
+    d = _tdesc(**kw)
+    assert la.longattn_tglobal_workspace_size(d)[0] == status
+    assert la.longattn_tglobal_side(d, *([FAKE] * 7), FAKE, 1 << 30, None) == status
+    assert la.longattn_tglobal_forward(d, *([FAKE] * 10), FAKE, 1 << 30, None) == status
+
+
+def test_tglobal_workspace_covers_both_calls():
+    # max(B*G*d_model aggregates, H*(2*(r+191)+1 + 2*md+1) bias entries) floats
+    st, nbytes = la.longattn_tglobal_workspace_size(_tdesc())
+    assert st == la.LONGATTN_OK and nbytes == max(1024 * 512, 8 * (2 * 318 + 1 + 257)) * 4
+    st, nbytes = la.longattn_tglobal_workspace_size(_tdesc(n=100, d_model=64))
+    assert nbytes == max(6 * 64, 8 * (2 * (99 + 191) + 1 + 257)) * 4  # radius clamps to n - 1
+    assert la.longattn_tglobal_workspace_size(_tdesc(d_model=96))[0] == la.LONGATTN_ERR_UNSUPPORTED
+    d = _tdesc()
+    assert la.longattn_tglobal_side(d, *([FAKE] * 7), None, 0, None) == la.LONGATTN_ERR_WORKSPACE
+    assert la.longattn_tglobal_forward(d, *([FAKE] * 10), FAKE, nbytes - 1, None) == \
+        la.LONGATTN_ERR_WORKSPACE
+    assert la.longattn_tglobal_forward(d, FAKE + 2, *([FAKE] * 9), FAKE, 1 << 30, None) == \
+        la.LONGATTN_ERR_ALIGNMENT
+    assert la.longattn_tglobal_side(_tdesc(batch=0), *([None] * 7), None, 0, None) == \
+        la.LONGATTN_OK

@@ -1,0 +1,170 @@
+"""GPU parity of LongT5 Transient-Global attention against the fp64 oracle.
+
+Three comparisons: the global tokens' keys and values (side pass), the attention kernel on
+given global tokens (seeded bf16 side keys/values, so both sides read identical inputs), and the
+whole pipeline.  Tolerance, elementwise |gpu - oracle| <= atol + rtol * |oracle|, bf16 outputs:
+(2e-2, 1e-2); lse within 2e-3 (fp32 scores) for the attention on given global tokens.  End to
+end, the global tokens' keys are stored in bf16 before the attention reads them (relative error
+2^-9 per element), which moves a side score by up to scale * |q| |side_k| 2^-9 (about 0.016 for
+d = 64 with unit-variance rows); a row with few keys carries that into its lse, so the pipeline's
+lse bar is 1e-2.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_long_sequence_banded_amd as la
+from workloads.gen import bf16_bits_to_f32, round_to_bf16_bits
+from workloads.tglobal import (TG_WORKLOADS, make_tglobal_inputs, tglobal_to_torch,
+                               tglobal_workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_ATOL, LSE_ATOL_PIPELINE = 2e-2, 1e-2, 2e-3, 1e-2
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.load()
+    yield
+
+
+def _close(got, ref, label, atol=ATOL, rtol=RTOL):
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    assert not bad.any(), f"{label}: {int(bad.sum())} out of tolerance, max-abs {err.max():.3e}"
+    return float(err.max()) if err.size else 0.0
+
+
+def _lse_close(got, ref, label, tol=LSE_ATOL):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{label}: lse finiteness"
+    if fin.any():
+        e = float(np.abs(got[fin] - ref[fin]).max())
+        assert e <= tol, f"{label}: lse error {e:.3e}"
+
+
+def _to_np(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.cpu().view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_gpu(inp, side=None):
+    """Whole pipeline, or the attention alone on the given (side_k, side_v, side_valid) bits."""
+    import torch
+
+    t = tglobal_to_torch(inp, "cuda:0")
+    kw = dict(radius=inp.radius, block=inp.block, scale=inp.scale, num_buckets=inp.num_buckets,
+              max_distance=inp.max_distance, eps=inp.eps, key_pad=t["key_pad"])
+    if side is None:
+        out, lse, sk, sv, valid = la.tglobal(t["x"], t["gamma"], t["wk"], t["wv"], t["q"],
+                                             t["k"], t["v"], t["bias_local"], t["bias_side"],
+                                             **kw)
+    else:
+        sk_b, sv_b, valid_np = side
+        sk = torch.from_numpy(sk_b.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        sv = torch.from_numpy(sv_b.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        valid = torch.from_numpy(valid_np).to("cuda:0")
+        desc = la.make_tglobal_desc(t["q"], d_model=inp.d_model, **kw)
+        st, wsb = la.longattn_tglobal_workspace_size(desc)
+        assert st == 0
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda:0")
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda:0")
+        st = la.longattn_tglobal_forward(desc, t["q"].data_ptr(), t["k"].data_ptr(),
+                                         t["v"].data_ptr(), sk.data_ptr(), sv.data_ptr(),
+                                         valid.data_ptr(), t["bias_local"].data_ptr(),
+                                         t["bias_side"].data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), ws.data_ptr(), wsb, None)
+        assert st == 0, la.longattn_status_string(st)
+    torch.cuda.synchronize()
+    return _to_np(out), lse.cpu().numpy().astype(np.float64), _to_np(sk), _to_np(sv), \
+        valid.cpu().numpy()
+
+
+def oracle_attention(inp, sk, sv, valid, heads=None):
+    hs = list(range(inp.heads)) if heads is None else list(heads)
+    return oracle.tglobal_forward(inp.f64("q")[:, hs], inp.f64("k")[:, hs], inp.f64("v")[:, hs],
+                                  sk[:, hs], sv[:, hs], valid, radius=inp.radius,
+                                  block=inp.block, num_buckets=inp.num_buckets,
+                                  max_distance=inp.max_distance, scale=inp.scale,
+                                  bias_local=inp.bias_local[:, hs],
+                                  bias_side=inp.bias_side[:, hs], key_pad=inp.key_pad)
+
+
+CASES = [
+    dict(batch=2, heads=2, n=1000, d=64, d_model=64, radius=127, block=16, pad_tail=(0, 77)),
+    dict(batch=1, heads=3, n=257, d=128, d_model=192, radius=5, block=4),
+    dict(batch=2, heads=1, n=17, d=64, d_model=64, radius=0, block=16, pad_tail=(3, 0)),
+    dict(batch=1, heads=2, n=1, d=64, d_model=64, radius=127, block=16),
+    dict(batch=1, heads=2, n=600, d=64, d_model=64, radius=300, block=64, num_buckets=64,
+         max_distance=400),
+    dict(batch=2, heads=2, n=333, d=128, d_model=128, radius=31, block=16, num_buckets=4,
+         max_distance=8, pad_tail=(40, 333 - 20)),
+]
+
+
+@pytest.mark.parametrize("kw", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_tglobal_pipeline_parity(kw):
+    _note(f"[tglobal] {kw}")
+    inp = make_tglobal_inputs(90 + len(str(kw)), **kw)
+    out, lse, sk, sv, valid = run_gpu(inp)
+    ref_out, ref_lse, _, rsk, rsv, rvalid = oracle.tglobal_inputs(inp)
+    assert np.array_equal(valid, rvalid)
+    e1 = _close(sk, rsk, "side_k")
+    e2 = _close(sv, rsv, "side_v")
+    e3 = _close(out, ref_out, "out")
+    _lse_close(lse, ref_lse, "lse", LSE_ATOL_PIPELINE)
+    _note(f"[tglobal] side max-abs {max(e1, e2):.3e}, out max-abs {e3:.3e}")
+
+
+@pytest.mark.parametrize("kw", CASES[:3], ids=["a0", "a1", "a2"])
+def test_tglobal_attention_on_given_global_tokens(kw):
+    """The attention kernel alone, on seeded bf16 global tokens (every other one invalid)."""
+    inp = make_tglobal_inputs(95, **kw)
+    G = max(1, inp.n // inp.block)
+    rng = np.random.default_rng(96)
+    sk_b = round_to_bf16_bits(rng.standard_normal((inp.batch, inp.heads, G, inp.d),
+                                                  dtype=np.float32))
+    sv_b = round_to_bf16_bits(rng.standard_normal((inp.batch, inp.heads, G, inp.d),
+                                                  dtype=np.float32))
+    valid = (np.arange(G)[None, :] % 2 == 0).repeat(inp.batch, 0).astype(np.uint8)
+    out, lse, *_ = run_gpu(inp, side=(sk_b, sv_b, valid))
+    ref_out, ref_lse, _ = oracle_attention(inp, bf16_bits_to_f32(sk_b).astype(np.float64),
+                                           bf16_bits_to_f32(sv_b).astype(np.float64), valid)
+    e = _close(out, ref_out, "out")
+    _lse_close(lse, ref_lse, "lse")
+    _note(f"[tglobal attention] max-abs {e:.3e}")
+
+
+def test_tglobal_full_size_sampled_heads():
+    wl = TG_WORKLOADS["tglobal_16k"]
+    _note(f"[tglobal] {wl.name} full launch, oracle on heads 0 and 5")
+    inp = tglobal_workload_inputs(wl)
+    out, lse, sk, sv, valid = run_gpu(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rsk, rsv, rvalid = oracle.tglobal_side(inp.f64("x"), inp.gamma, inp.f64("wk"),
+                                           inp.f64("wv"), heads=inp.heads, d=inp.d,
+                                           block=inp.block, eps=inp.eps, key_pad=inp.key_pad)
+    _close(sk, rsk, "side_k")
+    _close(sv, rsv, "side_v")
+    heads = [0, 5]
+    ref_out, ref_lse, _ = oracle_attention(inp, rsk, rsv, rvalid, heads)
+    e = _close(out[:, heads], ref_out, "out")
+    _lse_close(lse[:, heads], ref_lse, "lse", LSE_ATOL_PIPELINE)
+    _note(f"[tglobal] {wl.name}: max-abs {e:.3e}")
