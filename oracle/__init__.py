@@ -9,7 +9,8 @@ The arithmetic lives in ``longattn_oracle.c`` (plain C, fp64, OpenMP); what it c
 which passage each step follows is written at the top of that file.  ``decode_inputs`` states a
 decode step over a key/value cache as that same forward pass on the gathered window;
 ``backward`` gives the exact gradients of the forward pass; ``tglobal_side`` and
-``tglobal_forward`` state LongT5's Transient-Global attention.  Every function is pinned
+``tglobal_forward`` state LongT5's Transient-Global attention; ``gate_elementwise`` and
+``gate_lowrank`` the output gates of gated attention.  Every function is pinned
 by the CPU tests (dense brute force, library full/causal attention, the Big Bird worked window
 example, closed-form counts and invariants); none is left "parity unpinned".
 """
@@ -71,6 +72,10 @@ def _bind(lib):
         _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_double, _P, _P, _P, _P, _P, _P,
         _P, _P, _P, _P, _P, _P, ctypes.c_int,
     ]
+    lib.longattn_oracle_gate_elementwise.restype = ctypes.c_int
+    lib.longattn_oracle_gate_elementwise.argtypes = [_I64, _P, _P, _P]
+    lib.longattn_oracle_gate_lowrank.restype = ctypes.c_int
+    lib.longattn_oracle_gate_lowrank.argtypes = [_I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]
     lib.longattn_oracle_row_set.restype = ctypes.c_int64
     lib.longattn_oracle_row_set.argtypes = [
         _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64,
@@ -339,3 +344,33 @@ def tglobal_inputs(inp, nthreads: int = 0):
                                   bias_side=inp.bias_side, key_pad=inp.key_pad,
                                   nthreads=nthreads)
     return out, lse, E, sk, sv, valid
+
+
+# ---------------------------------------------------------------------- output gates
+def gate_elementwise(out: np.ndarray, gate: np.ndarray) -> np.ndarray:
+    """out * sigmoid(gate), elementwise (any matching shapes), fp64."""
+    o = np.ascontiguousarray(out, dtype=np.float64)
+    g = np.ascontiguousarray(gate, dtype=np.float64)
+    assert o.shape == g.shape
+    res = np.empty_like(o)
+    rc = _load().longattn_oracle_gate_elementwise(o.size, _ptr(o), _ptr(g), _ptr(res))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return res
+
+
+def gate_lowrank(out: np.ndarray, w_down: np.ndarray, w_up: np.ndarray) -> np.ndarray:
+    """out [B, H, n, d] gated by sigmoid(W_up (W_down o)) over each token's H*d outputs;
+    w_down [r, H*d], w_up [H*d, r]."""
+    o = np.ascontiguousarray(out, dtype=np.float64)
+    B, H, n, d = o.shape
+    wd = np.ascontiguousarray(w_down, dtype=np.float64)
+    wu = np.ascontiguousarray(w_up, dtype=np.float64)
+    r = wd.shape[0]
+    assert wd.shape == (r, H * d) and wu.shape == (H * d, r)
+    res = np.empty_like(o)
+    rc = _load().longattn_oracle_gate_lowrank(B, H, n, d, r, _ptr(o), _ptr(wd), _ptr(wu),
+                                              _ptr(res))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return res

@@ -566,3 +566,56 @@ int longattn_oracle_tglobal_forward(int64_t B, int64_t H, int64_t n, int64_t d, 
   if (E_out) *E_out = E;
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Output gates of gated attention (SWA/Hybrid-RoPE blog, section 3: Gated Attention).
+ *
+ * Elementwise: each head's output is multiplied, dimension by dimension, by a sigmoid gate:
+ *   gated[b][h][i][c] = out[b][h][i][c] * sigmoid(gate[b][h][i][c]),
+ * gate being the pre-sigmoid logits the model computes for that token (an input here).
+ * LowRank (bottleneck r, 128 on the page): the token's attention output over all heads,
+ * o = out[b][:][i][:] flattened head-major (H*d values), is projected to r dimensions and back,
+ * and the result gates o:  gated = o * sigmoid(W_up (W_down o)), W_down: [r][H*d],
+ * W_up: [H*d][r].  sigmoid(x) = 1 / (1 + exp(-x)).  fp64.
+ * ------------------------------------------------------------------------------------------ */
+int longattn_oracle_gate_elementwise(int64_t count, const double* out, const double* gate,
+                                     double* gated) {
+  if (count < 0 || !out || !gate || !gated) return ORACLE_BAD_ARG;
+  for (int64_t e = 0; e < count; ++e) gated[e] = out[e] / (1.0 + exp(-gate[e]));
+  return ORACLE_OK;
+}
+
+int longattn_oracle_gate_lowrank(int64_t B, int64_t H, int64_t n, int64_t d, int64_t r,
+                                 const double* out, const double* w_down, const double* w_up,
+                                 double* gated) {
+  if (B < 0 || H < 1 || n < 0 || d < 1 || r < 1 || !out || !w_down || !w_up || !gated)
+    return ORACLE_BAD_ARG;
+  const int64_t hd = H * d;
+  double* o = (double*)malloc((size_t)hd * sizeof(double));
+  double* z = (double*)malloc((size_t)r * sizeof(double));
+  if (!o || !z) {
+    free(o);
+    free(z);
+    return ORACLE_NO_MEMORY;
+  }
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t i = 0; i < n; ++i) {
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t c = 0; c < d; ++c) o[h * d + c] = out[((b * H + h) * n + i) * d + c];
+      for (int64_t t = 0; t < r; ++t) {
+        double acc = 0.0;
+        for (int64_t e = 0; e < hd; ++e) acc += w_down[t * hd + e] * o[e];
+        z[t] = acc;
+      }
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t c = 0; c < d; ++c) {
+          const int64_t e = h * d + c;
+          double acc = 0.0;
+          for (int64_t t = 0; t < r; ++t) acc += w_up[e * r + t] * z[t];
+          gated[((b * H + h) * n + i) * d + c] = o[e] / (1.0 + exp(-acc));
+        }
+    }
+  free(o);
+  free(z);
+  return ORACLE_OK;
+}
