@@ -4,6 +4,7 @@
     python bench.py --decode swa512_decode_32k [--steps K] [--warmup W]
     python bench.py --backward [--workload NAME] [--steps K] [--warmup W]
     python bench.py --tglobal tglobal_16k [--steps K] [--warmup W]
+    python bench.py --gates [--workload NAME] [--steps K] [--warmup W]
 
 One step is one full forward pass (global-row partials, main sparse kernel, global-row combine)
 over the workload's seeded synthetic inputs, already resident in device memory.  K steps are
@@ -48,6 +49,10 @@ def _parse():
     ap.add_argument("--tglobal", default=None, metavar="NAME",
                     help="instead of the forward bench: time LongT5 Transient-Global attention "
                          "(global-token pass + attention) on the named workload (tglobal_16k)")
+    ap.add_argument("--gates", action="store_true",
+                    help="instead of the forward bench: time the forward pass with the fused "
+                         "elementwise output gate against the plain one (workload given by "
+                         "--workload), and the low-rank gate (r = 128) on that workload's output")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the attention bench: time K device-to-device copies of this "
                          "many MiB (a kernel of known HBM traffic, used to calibrate the "
@@ -412,6 +417,76 @@ def _tglobal_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _gates_bench(args):
+    """Gated attention's output gates.  The elementwise gate is fused into the forward pass: the
+    line gives the gated step time and its overhead over the plain step.  The low-rank gate
+    (bottleneck 128) reads every output twice and writes it once; value = its HBM throughput
+    (3 * output bytes + weights) per step."""
+    import numpy as np
+    import torch
+
+    import sparse_long_sequence_banded_amd as la
+    from workloads import make_inputs, workload
+    from workloads.gates import gate_logits, lowrank_inputs
+    from workloads.torch_io import to_torch
+
+    w = workload(args.workload)
+    inp = make_inputs(w)
+    t = to_torch(inp, "cuda:0")
+    kw = dict(scale=inp.scale, win_left=inp.win_left, win_right=inp.win_right,
+              dilation=inp.dilation, global_idx=t["global_idx"], key_pad=t["key_pad"],
+              block_layout=t["layout"], block=inp.block)
+    g = torch.from_numpy(gate_logits(inp.q.shape, 500).view(np.int16)).view(
+        torch.bfloat16).to("cuda:0")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda:0")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    plain_ms = timed(lambda: la.forward(t["q"], t["k"], t["v"], out=out, lse=lse, **kw))
+    gated_ms = timed(lambda: la.forward(t["q"], t["k"], t["v"], out=out, lse=lse, gate=g, **kw))
+    B, H, n, d = inp.q.shape
+    r = 128
+    o, wd, wu = lowrank_inputs(7, batch=B, heads=H, n=n, d=d, rank=r)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    ob, wdb, wub = dev(o), dev(wd), dev(wu)
+    lr_ms = timed(lambda: la.gate_lowrank(ob, wdb, wub))
+    nbytes = 3 * ob.numel() * 2 + 2 * wdb.numel() * 2
+    value = nbytes / (lr_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "output gates of gated attention: low-rank gate HBM throughput; fused "
+                  "elementwise gate overhead on the forward step",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(lr_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "lowrank_rank": r, "tokens": B * n, "hd": H * d,
+                   "lowrank_flop": 4.0 * B * n * H * d * r},
+        "forward_ms": {"plain": round(plain_ms, 5), "gated": round(gated_ms, 5),
+                       "overhead_pct": round(100.0 * (gated_ms - plain_ms) / plain_ms, 2)},
+        "roofline": {"bound": "hbm", "kernel": "gate_lowrank_kernel (whole call)",
+                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def _source_hash():
     with open(MAIN_KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -479,6 +554,9 @@ def main():
         return
     if args.tglobal:
         _tglobal_bench(args)
+        return
+    if args.gates:
+        _gates_bench(args)
         return
 
     import numpy as np

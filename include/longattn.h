@@ -106,6 +106,29 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
                                         size_t workspace_bytes, void* stream,
                                         void* const* marks, int32_t n_marks);
 
+/* The forward pass of gated attention with an elementwise output gate (SWA/Hybrid-RoPE blog,
+ * section 3, Gated Attention: a per-dimension sigmoid gate on each head's output), fused into
+ * the kernels' epilogues: out = attention(q, k, v) * sigmoid(gate), elementwise.  gate: DEVICE
+ * [B][H][n][d] pre-sigmoid logits in desc->dtype (not NULL, 16-byte aligned); lse is that of the
+ * attention before the gate.  Everything else as longattn_forward. */
+longattn_status longattn_forward_gated(const longattn_desc* desc, const void* q, const void* k,
+                                       const void* v, const void* gate, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Low-rank output gate of gated attention (SWA/Hybrid-RoPE blog, section 3: the attention output
+ * is projected to a bottleneck, 128 dimensions on the page, and then gates): for every token,
+ * o = its outputs over all heads (H*d values, head-major), and
+ *   out = o * sigmoid(w_up (w_down o)),
+ * written in place.  out: DEVICE bf16 [B][H][n][d]; w_down: DEVICE bf16 [rank][H*d]; w_up:
+ * DEVICE bf16 [H*d][rank]; 16-byte aligned.  Kernels: d % 16 == 0, H*d % 32 == 0 and
+ * H*d <= 16384, rank in {32, 64, 128, 256}; other valid sizes return UNSUPPORTED. */
+typedef struct {
+  int32_t batch, heads, n, d;
+  int32_t rank;
+} longattn_gate_desc;
+longattn_status longattn_gate_lowrank(const longattn_gate_desc* desc, void* out,
+                                      const void* w_down, const void* w_up, void* stream);
+
 /* Useful score entries, counted on the GPU: entries_out is a DEVICE int64[2] that receives
  * [0] E = sum over all (b, h, i) of |S(b, h, i)| and [1] the part of E in global-token rows
  * (asynchronous on `stream`).  4 * d * E is the useful floating-point work of one forward pass

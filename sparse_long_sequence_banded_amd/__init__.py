@@ -36,9 +36,11 @@ EXPORTED = (
     "longattn_forward",
     "longattn_forward_marked",
     "longattn_count_entries",
+    "longattn_forward_gated",
     "longattn_backward_workspace_size",
     "longattn_backward",
     "longattn_backward_marked",
+    "longattn_gate_lowrank",
     "longattn_tglobal_workspace_size",
     "longattn_tglobal_side",
     "longattn_tglobal_forward",
@@ -106,6 +108,18 @@ class longattn_tglobal_desc(ctypes.Structure):
     ]
 
 
+class longattn_gate_desc(ctypes.Structure):
+    """Mirror of ``longattn_gate_desc`` in include/longattn.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+    ]
+
+
 class LongAttnNotBuilt(RuntimeError):
     pass
 
@@ -141,6 +155,8 @@ def load():
             lib.longattn_forward_marked.restype = ctypes.c_int
             lib.longattn_count_entries.argtypes = [D, P, P]
             lib.longattn_count_entries.restype = ctypes.c_int
+            lib.longattn_forward_gated.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.longattn_forward_gated.restype = ctypes.c_int
             lib.longattn_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
             lib.longattn_backward_workspace_size.restype = ctypes.c_int
             lib.longattn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -150,6 +166,8 @@ def load():
                                                      ctypes.POINTER(ctypes.c_void_p),
                                                      ctypes.c_int32]
             lib.longattn_backward_marked.restype = ctypes.c_int
+            lib.longattn_gate_lowrank.argtypes = [ctypes.POINTER(longattn_gate_desc), P, P, P, P]
+            lib.longattn_gate_lowrank.restype = ctypes.c_int
             TD = ctypes.POINTER(longattn_tglobal_desc)
             lib.longattn_tglobal_workspace_size.argtypes = [TD, ctypes.POINTER(ctypes.c_size_t)]
             lib.longattn_tglobal_workspace_size.restype = ctypes.c_int
@@ -200,6 +218,13 @@ def longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes,
 
 def longattn_count_entries(desc, entries_out, stream) -> int:
     return load().longattn_count_entries(ctypes.byref(desc), entries_out, stream)
+
+
+def longattn_forward_gated(desc, q, k, v, gate, out, lse, workspace, workspace_bytes,
+                           stream) -> int:
+    """Raw call of the forward pass with an elementwise output gate."""
+    return load().longattn_forward_gated(ctypes.byref(desc), q, k, v, gate, out, lse, workspace,
+                                         int(workspace_bytes), stream)
 
 
 def longattn_backward_workspace_size(desc: longattn_desc) -> Tuple[int, int]:
@@ -308,9 +333,10 @@ def make_desc(q, *, scale: Optional[float] = None, win_left: int = -1, win_right
 def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
             win_right: int = -1, dilation=None, global_idx=None, key_pad=None,
             block_layout=None, block: int = 0, out=None, lse=None, want_lse: bool = True,
-            workspace=None, stream=None, marks=None):
+            workspace=None, stream=None, marks=None, gate=None):
     """Banded / global / block-sparse attention forward on torch device tensors [B, H, n, d].
 
+    ``gate``: optional [B, H, n, d] logits of an elementwise output gate (out *= sigmoid(gate)).
     Returns (out, lse); lse is None when ``want_lse`` is False and no ``lse`` is given.
     """
     import torch
@@ -333,7 +359,15 @@ def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     sh = _stream_handle(stream)
-    if marks is None:
+    if gate is not None:
+        if gate.shape != q.shape or gate.dtype != q.dtype or not gate.is_contiguous():
+            raise ValueError("gate must be a contiguous tensor of q's shape and dtype")
+        if marks is not None:
+            raise ValueError("marks are not available with a gate")
+        st = longattn_forward_gated(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    gate.data_ptr(), out.data_ptr(), _ptr(lse),
+                                    _ptr(workspace) if ws_bytes else None, ws_bytes, sh)
+    elif marks is None:
         st = longattn_forward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               _ptr(lse), _ptr(workspace) if ws_bytes else None, ws_bytes, sh)
     else:
@@ -550,3 +584,25 @@ def tglobal(x, gamma, wk, wv, q, k, v, bias_local, bias_side, *, radius: int = 1
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_tglobal_forward")
     return out, lse, side_k, side_v, side_valid
+
+
+def longattn_gate_lowrank(desc: longattn_gate_desc, out, w_down, w_up, stream) -> int:
+    return load().longattn_gate_lowrank(ctypes.byref(desc), out, w_down, w_up, stream)
+
+
+def gate_lowrank(out, w_down, w_up, stream=None):
+    """Gate ``out`` [B, H, n, d] (bf16, in place) by sigmoid(w_up (w_down o)) over each token's
+    H*d outputs; w_down [r, H*d], w_up [H*d, r] bf16.  Returns ``out``."""
+    for t in (out, w_down, w_up):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("out, w_down, w_up must be contiguous device tensors")
+    B, H, n, d = out.shape
+    r = w_down.shape[0]
+    if w_down.shape != (r, H * d) or w_up.shape != (H * d, r):
+        raise ValueError("w_down must be [r, H*d] and w_up [H*d, r]")
+    desc = longattn_gate_desc(batch=B, heads=H, n=n, d=d, rank=r)
+    st = longattn_gate_lowrank(desc, out.data_ptr(), w_down.data_ptr(), w_up.data_ptr(),
+                               _stream_handle(stream))
+    if st != LONGATTN_OK:
+        raise LongAttnError(st, "longattn_gate_lowrank")
+    return out

@@ -24,6 +24,7 @@ struct FwdCore {
   const uint8_t* kpad;    // [B][n] or null
   const int32_t* layout;  // [H][n/block][max_kb] or null
   float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
+  const uint16_t* gate;   // elementwise output-gate logits [B][H][n][d] (out *= sigmoid), or null
   int B, H, n, g;
   int wl, wr;             // window extents clamped to n; band_on == 0 means no window
   int band_on;
@@ -108,6 +109,14 @@ struct TgArgs {
   float scale_log2, eps;
 };
 
+// Low-rank output gate.
+struct GateArgs {
+  uint16_t* out;            // [B][H][n][d], gated in place
+  const uint16_t* w_down;   // [r][H*d]
+  const uint16_t* w_up;     // [H*d][r]
+  int B, H, n, d, r;
+};
+
 // Launchers (defined next to their kernels).
 int main_rows_per_workgroup(int mode, int d, int block);
 // Optional events that record a kernel's own start and end (attached to its dispatch).
@@ -133,5 +142,6 @@ hipError_t launch_tglobal_side(const TgArgs& a, const uint16_t* x, const float* 
                                hipStream_t s);
 hipError_t launch_tglobal_attention(const TgArgs& a, const float* tab_local,
                                     const float* tab_side, hipStream_t s);
+hipError_t launch_gate_lowrank(const GateArgs& a, hipStream_t s);
 
 }  // namespace longattn

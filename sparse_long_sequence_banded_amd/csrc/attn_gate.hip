@@ -1,0 +1,147 @@
+// Low-rank output gate of gated attention (SWA/Hybrid-RoPE blog, section 3, Gated Attention:
+// the attention output goes through a 128-dimension bottleneck and then gates): for every token,
+// o = its outputs over all heads (H*d values, head-major), z = W_down o (r values),
+// out = o * sigmoid(W_up z), in place.
+//
+// One wave gates 32 tokens (a workgroup of four waves, 128 tokens, shares the weights through
+// LDS) with two chained products on 32x32x16 bf16 MFMA (fp32 sums):
+//   Z^T [r x 32] = W_down [r x Hd] O^T [Hd x 32]   (A: W_down rows; B: the tokens' output rows)
+//   G^T [Hd x 32] = W_up [Hd x r] Z^T [r x 32]     (B: Z^T straight from the first product's
+//                                                  accumulators, rounded to bf16)
+// The accumulator layout gives lane half hh the bottleneck rows 4hh + {0..3} and 8 + 4hh + {0..3}
+// of each 16-row step, so the second product's A operands (W_up rows) are read in that order.
+// Every token is read and written by one wave only, so the update in place is safe.
+
+#include "attn_args.h"
+#include "mfma_util.h"
+
+namespace longattn {
+namespace {
+
+using namespace mfma;
+
+// LDS rows are padded by 16 bytes so that the 32 rows a wave reads land in different banks.
+constexpr int kGateKChunk = 64;                  // W_down columns per staged chunk
+constexpr int kGateDownRow = kGateKChunk + 8;    // padded row length (bf16)
+
+template <int R>
+__global__ __launch_bounds__(256) void gate_lowrank_kernel(GateArgs a) {
+  constexpr int ZB = R / 32;  // 32-row blocks of Z^T
+  constexpr int UPROW = R + 8;  // padded W_up row (bf16)
+  // one buffer, used for W_down chunks [R][64] during the first product and for W_up row blocks
+  // [32][R] during the second
+  constexpr int kElems = (R * kGateDownRow > 32 * UPROW) ? R * kGateDownRow : 32 * UPROW;
+  __shared__ __attribute__((aligned(16))) uint16_t wsm[kElems];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qj = lane & 31, hh = lane >> 5;
+  const long tokens = (long)a.B * a.n;
+  const long tok = ((long)blockIdx.x * 4 + wave) * 32 + qj;  // this lane's token (B operand col)
+  const bool tok_ok = tok < tokens;
+  const long tb = tok_ok ? tok / a.n : 0, ti = tok_ok ? tok % a.n : 0;
+  const int Hd = a.H * a.d;
+  // element e = h*d + c of this token's outputs
+  auto optr = [&](int e) -> uint16_t* {
+    return a.out + ((tb * a.H + e / a.d) * a.n + ti) * a.d + e % a.d;
+  };
+
+  // ---- Z^T = W_down O^T, W_down staged 64 columns at a time
+  f32x16 z[ZB];
+#pragma unroll
+  for (int zb = 0; zb < ZB; ++zb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[zb][r] = 0.f;
+  for (int k0 = 0; k0 < Hd; k0 += kGateKChunk) {
+    // this chunk's output rows of the token (loaded before the barrier, used after it)
+    u32x4 bo[kGateKChunk / 16];
+#pragma unroll
+    for (int ks = 0; ks < kGateKChunk / 16; ++ks) {
+      bo[ks] = u32x4{0, 0, 0, 0};
+      if (tok_ok && k0 + 16 * ks < Hd) bo[ks] = *reinterpret_cast<const u32x4*>(optr(k0 + 16 * ks + 8 * hh));
+    }
+    __syncthreads();  // the previous chunk is consumed
+    for (int e = tid; e < R * (kGateKChunk / 8); e += 256) {
+      const int row = e / (kGateKChunk / 8), c8 = e % (kGateKChunk / 8);
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (k0 + 8 * c8 < Hd) v = *reinterpret_cast<const u32x4*>(a.w_down + (long)row * Hd + k0 + 8 * c8);
+      *reinterpret_cast<u32x4*>(&wsm[row * kGateDownRow + 8 * c8]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kGateKChunk / 16; ++ks)
+#pragma unroll
+      for (int zb = 0; zb < ZB; ++zb) {
+        const u32x4 aw = *reinterpret_cast<const u32x4*>(&wsm[(32 * zb + qj) * kGateDownRow + 16 * ks + 8 * hh]);
+        z[zb] = mfma_32x32x16(aw, bo[ks], z[zb]);
+      }
+  }
+  // Z^T as bf16 B operands: step s (rows 16s .. 16s+15) uses accumulator block s/2, registers
+  // 8(s%2) .. 8(s%2)+7
+  uint32_t zp[ZB][8];
+#pragma unroll
+  for (int zb = 0; zb < ZB; ++zb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zp[zb][j] = pack_bf16x2(z[zb][2 * j], z[zb][2 * j + 1]);
+
+  // ---- G^T = W_up Z^T, one 32-row block of the outputs at a time (W_up rows staged), then
+  // the gate
+  for (int ob = 0; ob < Hd; ob += 32) {
+    // the outputs this lane gates in this block, loaded ahead of the barrier
+    u32x2 ov[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      ov[q4] = u32x2{0, 0};
+      if (tok_ok) ov[q4] = *reinterpret_cast<const u32x2*>(optr(ob + 8 * q4 + 4 * hh));
+    }
+    __syncthreads();
+    for (int e = tid; e < 32 * (R / 8); e += 256) {
+      const int row = e / (R / 8), c8 = e % (R / 8);
+      *reinterpret_cast<u32x4*>(&wsm[row * UPROW + 8 * c8]) =
+          *reinterpret_cast<const u32x4*>(a.w_up + (long)(ob + row) * R + 8 * c8);
+    }
+    __syncthreads();
+    f32x16 g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g[r] = 0.f;
+    const uint16_t* wrow = &wsm[qj * UPROW];
+#pragma unroll
+    for (int s = 0; s < R / 16; ++s) {
+      const int rb = 16 * s;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + rb + 4 * hh);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + rb + 8 + 4 * hh);
+      const int zb = s >> 1, j0 = 4 * (s & 1);
+      g = mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                        u32x4{zp[zb][j0], zp[zb][j0 + 1], zp[zb][j0 + 2], zp[zb][j0 + 3]}, g);
+    }
+    if (!tok_ok) continue;
+    // lane (token, hh) holds output rows ob + 8(j/4) + 4hh + j%4: four runs of 4 consecutive
+    // elements of one head
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 w;
+      w[0] = pack_bf16x2(bf16_lo(ov[q4][0]) * sigmoid_fast(g[4 * q4]),
+                         bf16_hi(ov[q4][0]) * sigmoid_fast(g[4 * q4 + 1]));
+      w[1] = pack_bf16x2(bf16_lo(ov[q4][1]) * sigmoid_fast(g[4 * q4 + 2]),
+                         bf16_hi(ov[q4][1]) * sigmoid_fast(g[4 * q4 + 3]));
+      *reinterpret_cast<u32x2*>(optr(ob + 8 * q4 + 4 * hh)) = w;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_lowrank(const GateArgs& a, hipStream_t s) {
+  const long tokens = (long)a.B * a.n;
+  if (tokens <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((tokens + 127) / 128));
+  switch (a.r) {
+    case 32: hipLaunchKernelGGL(gate_lowrank_kernel<32>, grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(gate_lowrank_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(gate_lowrank_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(gate_lowrank_kernel<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace longattn

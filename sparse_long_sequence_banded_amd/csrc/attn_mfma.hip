@@ -735,14 +735,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
       } else {
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
         uint16_t* orow = a.out + (bh * a.n + qpos[qb]) * D;
+        // elementwise output gate (gated attention): out *= sigmoid(gate logits)
+        const uint16_t* grow = a.gate ? a.gate + (bh * a.n + qpos[qb]) * D : nullptr;
   #pragma unroll
         for (int db = 0; db < DB; ++db)
   #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             const int d = 32 * db + 8 * rq + 4 * hh;
+            float y0 = o[qb][db][4 * rq] * inv, y1 = o[qb][db][4 * rq + 1] * inv;
+            float y2 = o[qb][db][4 * rq + 2] * inv, y3 = o[qb][db][4 * rq + 3] * inv;
+            if (grow) {
+              const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d);
+              y0 *= sigmoid_fast(bf16_lo(gw[0]));
+              y1 *= sigmoid_fast(bf16_hi(gw[0]));
+              y2 *= sigmoid_fast(bf16_lo(gw[1]));
+              y3 *= sigmoid_fast(bf16_hi(gw[1]));
+            }
             u32x2 w;
-            w[0] = pack_bf16x2(o[qb][db][4 * rq] * inv, o[qb][db][4 * rq + 1] * inv);
-            w[1] = pack_bf16x2(o[qb][db][4 * rq + 2] * inv, o[qb][db][4 * rq + 3] * inv);
+            w[0] = pack_bf16x2(y0, y1);
+            w[1] = pack_bf16x2(y2, y3);
             *reinterpret_cast<u32x2*>(orow + d) = w;
           }
         if (a.lse && hh == 0)
@@ -824,10 +835,16 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     uint16_t* orow = a.out + (bh * a.n + pos) * D + 4 * t;
-    orow[0] = __builtin_bit_cast(uint16_t, (__bf16)(o.x * inv));
-    orow[1] = __builtin_bit_cast(uint16_t, (__bf16)(o.y * inv));
-    orow[2] = __builtin_bit_cast(uint16_t, (__bf16)(o.z * inv));
-    orow[3] = __builtin_bit_cast(uint16_t, (__bf16)(o.w * inv));
+    float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    if (a.gate) {  // elementwise output gate
+      const u32x2 gw = *reinterpret_cast<const u32x2*>(a.gate + (bh * a.n + pos) * D + 4 * t);
+      y[0] *= sigmoid_fast(bf16_lo(gw[0]));
+      y[1] *= sigmoid_fast(bf16_hi(gw[0]));
+      y[2] *= sigmoid_fast(bf16_lo(gw[1]));
+      y[3] *= sigmoid_fast(bf16_hi(gw[1]));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = __builtin_bit_cast(uint16_t, (__bf16)y[e]);
     if (a.lse && t == 0) a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
 }

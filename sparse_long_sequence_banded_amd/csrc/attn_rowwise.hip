@@ -66,7 +66,14 @@ __global__ __launch_bounds__(256) void rowwise_f32_kernel(FwdArgs a, int d) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int col = lane + 64 * e;
-    if (col < d) out[col] = acc[e] * inv;
+    if (col < d) {
+      float y = acc[e] * inv;
+      if (a.gate) {  // elementwise output gate: out *= sigmoid(gate logits)
+        const float g = reinterpret_cast<const float*>(a.gate)[row * d + col];
+        y = y / (1.f + expf(-g));
+      }
+      out[col] = y;
+    }
   }
   if (a.lse && lane == 0) a.lse[row] = (l > 0.f) ? m + logf(l) : -__builtin_inff();
 }

@@ -362,10 +362,14 @@ longattn_status longattn_workspace_size(const longattn_desc* desc, size_t* bytes
   return LONGATTN_OK;
 }
 
-longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
-                                        const void* v, void* out, float* lse, void* workspace,
-                                        size_t workspace_bytes, void* stream,
-                                        void* const* marks, int32_t n_marks) {
+}  // extern "C"
+
+namespace {
+
+longattn_status forward_impl(const longattn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* gate, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* marks, int32_t n_marks) {
   if (n_marks != 0 && n_marks != LONGATTN_N_MARKS) return LONGATTN_ERR_INVALID_ARG;
   if (n_marks && !marks) return LONGATTN_ERR_INVALID_ARG;
   Plan p;
@@ -384,6 +388,7 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   if (!q || !k || !v || !out) return LONGATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return LONGATTN_ERR_ALIGNMENT;
+  if (gate && !aligned16(gate)) return LONGATTN_ERR_ALIGNMENT;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return LONGATTN_ERR_WORKSPACE;
   if (debug_enabled()) {
     st = debug_check(desc, s);
@@ -400,6 +405,7 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   a.kpad = desc->key_pad;
   a.layout = desc->block_layout;
   a.part = static_cast<float*>(workspace);
+  a.gate = static_cast<const uint16_t*>(gate);
 
   // bf16: one launch computes every non-global row and, in extra workgroups, the global rows'
   // per-chunk partials; the combine then writes the global rows (overwriting what the main work
@@ -423,11 +429,31 @@ longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q
   return LONGATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+longattn_status longattn_forward_marked(const longattn_desc* desc, const void* q, const void* k,
+                                        const void* v, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        void* const* marks, int32_t n_marks) {
+  return forward_impl(desc, q, k, v, nullptr, out, lse, workspace, workspace_bytes, stream,
+                      marks, n_marks);
+}
+
 longattn_status longattn_forward(const longattn_desc* desc, const void* q, const void* k,
                                  const void* v, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  return longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes, stream,
-                                 nullptr, 0);
+  return forward_impl(desc, q, k, v, nullptr, out, lse, workspace, workspace_bytes, stream,
+                      nullptr, 0);
+}
+
+longattn_status longattn_forward_gated(const longattn_desc* desc, const void* q, const void* k,
+                                       const void* v, const void* gate, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate) return LONGATTN_ERR_INVALID_ARG;
+  return forward_impl(desc, q, k, v, gate, out, lse, workspace, workspace_bytes, stream,
+                      nullptr, 0);
 }
 
 longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entries_out,
@@ -532,6 +558,34 @@ longattn_status longattn_backward(const longattn_desc* desc, const void* q, cons
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return longattn_backward_marked(desc, q, k, v, out, lse, dout, dq, dk, dv, workspace,
                                   workspace_bytes, stream, nullptr, 0);
+}
+
+longattn_status longattn_gate_lowrank(const longattn_gate_desc* desc, void* out,
+                                      const void* w_down, const void* w_up, void* stream) {
+  if (!desc) return LONGATTN_ERR_INVALID_ARG;
+  if (desc->batch < 0 || desc->heads < 1 || desc->n < 0 || desc->d < 1 || desc->rank < 1)
+    return LONGATTN_ERR_INVALID_ARG;
+  const long hd = (long)desc->heads * desc->d;
+  if (desc->d % 16 != 0 || hd % 32 != 0 || hd > 16384) return LONGATTN_ERR_UNSUPPORTED;
+  if (desc->rank != 32 && desc->rank != 64 && desc->rank != 128 && desc->rank != 256)
+    return LONGATTN_ERR_UNSUPPORTED;
+  const long tokens = (long)desc->batch * desc->n;
+  if (tokens * hd > (1L << 46) || (tokens + 127) / 128 > 0x7fffffffL)
+    return LONGATTN_ERR_UNSUPPORTED;
+  if (tokens == 0) return LONGATTN_OK;
+  if (!out || !w_down || !w_up) return LONGATTN_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(w_down) || !aligned16(w_up)) return LONGATTN_ERR_ALIGNMENT;
+  GateArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.w_down = static_cast<const uint16_t*>(w_down);
+  a.w_up = static_cast<const uint16_t*>(w_up);
+  a.B = desc->batch;
+  a.H = desc->heads;
+  a.n = desc->n;
+  a.d = desc->d;
+  a.r = desc->rank;
+  const hipError_t e = launch_gate_lowrank(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LONGATTN_OK : LONGATTN_ERR_HIP;
 }
 
 longattn_status longattn_tglobal_workspace_size(const longattn_tglobal_desc* desc, size_t* bytes) {

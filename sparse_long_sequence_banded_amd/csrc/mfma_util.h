@@ -33,6 +33,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// sigmoid(x) = 1 / (1 + e^-x), from the hardware exp2 and reciprocal (saturates to 0 and 1).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_fast(-1.44269504088896340736f * x));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // s if bit `bit` of w is set, else ninf (which holds -inf): a sign-extended one-bit field
 // extract and a bitfield select.
 __device__ __forceinline__ float keep_if_bit(float s, uint32_t w, int bit, float ninf) {

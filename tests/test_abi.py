@@ -353,3 +353,48 @@ def test_tglobal_workspace_covers_both_calls():
         la.LONGATTN_ERR_ALIGNMENT
     assert la.longattn_tglobal_side(_tdesc(batch=0), *([None] * 7), None, 0, None) == \
         la.LONGATTN_OK
+
+
+# ------------------------------------------------------------------------------ output gates
+def test_gate_descriptor_layout_matches_the_header(tmp_path):
+    fields = [f for f, _ in la.longattn_gate_desc._fields_]
+    src = tmp_path / "glayout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "longattn.h"\nint main(void){\n'
+        + 'printf("%zu\\n", sizeof(longattn_gate_desc));\n'
+        + "".join(f'printf("%zu\\n", offsetof(longattn_gate_desc, {f}));\n' for f in fields)
+        + "return 0;}\n")
+    exe = tmp_path / "glayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(la.longattn_gate_desc)
+    assert vals[1:] == [getattr(la.longattn_gate_desc, f).offset for f in fields]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(rank=0), la.LONGATTN_ERR_INVALID_ARG),
+    (dict(rank=100), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(d=24), la.LONGATTN_ERR_UNSUPPORTED),
+    (dict(heads=3, d=16), la.LONGATTN_ERR_UNSUPPORTED),  # H*d not a multiple of 32
+])
+def test_bad_gate_descriptors_are_rejected(kw, status):
+    base = dict(batch=1, heads=16, n=100, d=64, rank=128)
+    base.update(kw)
+    d = la.longattn_gate_desc(**base)
+    assert la.longattn_gate_lowrank(d, FAKE, FAKE, FAKE, None) == status
+
+
+def test_gate_pointer_checks():
+    d = la.longattn_gate_desc(batch=1, heads=16, n=100, d=64, rank=128)
+    assert la.longattn_gate_lowrank(d, None, FAKE, FAKE, None) == la.LONGATTN_ERR_INVALID_ARG
+    assert la.longattn_gate_lowrank(d, FAKE + 8, FAKE, FAKE, None) == la.LONGATTN_ERR_ALIGNMENT
+    e = la.longattn_gate_desc(batch=0, heads=16, n=100, d=64, rank=128)
+    assert la.longattn_gate_lowrank(e, None, None, None, None) == la.LONGATTN_OK
+    f = _desc()
+    assert la.longattn_forward_gated(f, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == \
+        la.LONGATTN_ERR_INVALID_ARG
+    assert la.longattn_forward_gated(f, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None, None, 0, None) == \
+        la.LONGATTN_ERR_ALIGNMENT
