@@ -33,8 +33,10 @@ MAIN_KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", 
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU takes a few hundred microseconds of back-to-back work to reach its steady clock:
+    # the defaults time 500 steps after 100 warm-up steps (about 50 ms at dilated_16k)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-gflop", type=float, default=640.0,
@@ -148,7 +150,8 @@ def _decode_bench(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": _traffic_of("pmc_decode_swa512_decode_32k.json", "attn_decode.hip")
+            if wl.name == "swa512_decode_32k" else None,
         },
     }
     if not args.no_cpu_baseline:
@@ -492,17 +495,25 @@ def _source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(workload):
-    """HBM bytes per launch of the main kernel from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"pmc_main_kernel_{workload}.json")
+def _traffic_of(profile, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a copy kernel's readings), if it was taken on the current kernel
+    source (else None)."""
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != _source_hash():
+    with open(os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", source), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _traffic(workload):
+    """HBM bytes per launch of the main forward kernel (see _traffic_of)."""
+    return _traffic_of(f"pmc_main_kernel_{workload}.json", "attn_mfma.hip")
 
 
 def _cpu_baseline(inp, budget_gflop):
