@@ -39,6 +39,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-passes", type=int, default=50,
+                    help="forward passes timed one by one after a 512 MiB write that flushes "
+                         "L2 and the MALL (0 = skip)")
     ap.add_argument("--cpu-budget-gflop", type=float, default=640.0,
                     help="fp64 work of the oracle sample: whole heads (at least one); a workload "
                          "smaller than the budget is run repeatedly")
@@ -454,14 +457,32 @@ def _gates_bench(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / args.steps
 
-    plain_ms = timed(lambda: la.forward(t["q"], t["k"], t["v"], out=out, lse=lse, **kw))
-    gated_ms = timed(lambda: la.forward(t["q"], t["k"], t["v"], out=out, lse=lse, gate=g, **kw))
+    # raw C calls with the descriptor and pointers resolved once (as in the forward bench), so
+    # the host enqueues ahead of the GPU and the times are the GPU's
+    desc, keep = la.make_desc(t["q"], **kw)
+    _, ws_bytes = la.longattn_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    qkv = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr())
+    tail = (out.data_ptr(), lse.data_ptr(), ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+
+    def call(st, name):
+        if st != la.LONGATTN_OK:
+            raise la.LongAttnError(st, name)
+
+    plain_ms = timed(lambda: call(la.longattn_forward(desc, *qkv, *tail), "longattn_forward"))
+    gated_ms = timed(lambda: call(la.longattn_forward_gated(desc, *qkv, g.data_ptr(), *tail),
+                                  "longattn_forward_gated"))
     B, H, n, d = inp.q.shape
     r = 128
     o, wd, wu = lowrank_inputs(7, batch=B, heads=H, n=n, d=d, rank=r)
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
     ob, wdb, wub = dev(o), dev(wd), dev(wu)
-    lr_ms = timed(lambda: la.gate_lowrank(ob, wdb, wub))
+    gdesc = la.longattn_gate_desc(batch=B, heads=H, n=n, d=d, rank=r)
+    lr_ms = timed(lambda: call(la.longattn_gate_lowrank(gdesc, ob.data_ptr(), wdb.data_ptr(),
+                                                        wub.data_ptr(), sh),
+                               "longattn_gate_lowrank"))
+    del keep
     nbytes = 3 * ob.numel() * 2 + 2 * wdb.numel() * 2
     value = nbytes / (lr_ms * 1e-3) / 1e9
     rec = {
@@ -631,6 +652,28 @@ def main():
                       for s in range(args.steps)])  # ms
     attn_ms, comb_ms = (float(x) for x in spans.mean(axis=0))
     ms_per_step = elapsed * 1e3 / args.steps
+
+    # cold passes: before each, a 512 MiB write evicts the inputs from L2 and the MALL (the
+    # 256 MB last-level cache would otherwise hold a 134 MB working set); events bracket the
+    # forward alone on the launch stream
+    cold = None
+    if args.cold_passes > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_passes)]
+        for i, (e0, e1) in enumerate(ev):
+            flush.fill_(i & 0xFF)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        del flush
+        cold = {"passes": args.cold_passes, "flush_bytes": 512 << 20,
+                "ms_median": round(float(np.median(cms)), 5),
+                "ms_p10": round(float(np.percentile(cms, 10)), 5),
+                "ms_p90": round(float(np.percentile(cms, 90)), 5),
+                "tflops_median": round(4.0 * inp.d * E / (float(np.median(cms)) * 1e-3) / 1e12, 3)}
     useful_flop = 4.0 * inp.d * E
     value = useful_flop / (ms_per_step * 1e-3) / 1e12
 
@@ -665,6 +708,7 @@ def main():
             "description": w.note,
         },
         "pct_bf16_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "cold_l2_mall_flushed": cold,
         "kernels_ms": {"attention": round(attn_ms, 5),
                        "global_combine": round(comb_ms, 5) if inp.n_global else 0.0},
         "roofline": {
