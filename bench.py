@@ -426,8 +426,8 @@ def _tglobal_bench(args):
 def _gates_bench(args):
     """Gated attention's output gates.  The elementwise gate is fused into the forward pass: the
     line gives the gated step time and its overhead over the plain step.  The low-rank gate
-    (bottleneck 128) reads every output twice and writes it once; value = its HBM throughput
-    (3 * output bytes + weights) per step."""
+    (bottleneck 128) needs every output read and written once plus the two weight matrices;
+    value = those algorithmic bytes per second."""
     import numpy as np
     import torch
 
@@ -483,7 +483,7 @@ def _gates_bench(args):
                                                         wub.data_ptr(), sh),
                                "longattn_gate_lowrank"))
     del keep
-    nbytes = 3 * ob.numel() * 2 + 2 * wdb.numel() * 2
+    nbytes = 2 * ob.numel() * 2 + 2 * wdb.numel() * 2  # outputs read and written once, weights
     value = nbytes / (lr_ms * 1e-3) / 1e9
     rec = {
         "metric": "output gates of gated attention: low-rank gate HBM throughput; fused "

@@ -3,8 +3,8 @@
 // o = its outputs over all heads (H*d values, head-major), z = W_down o (r values),
 // out = o * sigmoid(W_up z), in place.
 //
-// One wave gates 32 tokens (a workgroup of four waves, 128 tokens, shares the weights through
-// LDS) with two chained products on 32x32x16 bf16 MFMA (fp32 sums):
+// General shapes: one wave gates 32 tokens (a workgroup of four waves, 128 tokens, shares the
+// weights through LDS) with two chained products on 32x32x16 bf16 MFMA (fp32 sums):
 //   Z^T [r x 32] = W_down [r x Hd] O^T [Hd x 32]   (A: W_down rows; B: the tokens' output rows)
 //   G^T [Hd x 32] = W_up [Hd x r] Z^T [r x 32]     (B: Z^T straight from the first product's
 //                                                  accumulators, rounded to bf16)
@@ -128,11 +128,148 @@ __global__ __launch_bounds__(256) void gate_lowrank_kernel(GateArgs a) {
   }
 }
 
+// The same gate when H*d = 256*NW (NW <= 8) and r <= 128: one workgroup of NW waves gates 32
+// tokens, wave w owning the 256 output elements [256w, 256w + 256) of each token, so the
+// launch has a workgroup per 32 tokens.
+//   Z^T: wave w multiplies its 256 columns of W_down with its outputs (a split of the sum over
+//   H*d), and the NW partial sums are added through LDS, one 32-row block of Z^T at a time.
+//   G^T: wave w computes its 256 rows, then gates its own outputs.
+// The order of the sum in the first product is free, so a lane's eight k-slots of 16-column step
+// s are taken as columns 16s + 4hh + {0..3} and 16s + 8 + 4hh + {0..3} (for A and B alike):
+// these are exactly the elements the accumulator layout of the second product puts in that lane
+// (rows 8q + 4hh + {0..3} of a 32-row block), so the outputs stay in registers between the two
+// products and are read from memory once.
+template <int NW, int R, int COLS>
+__global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a) {
+  constexpr int ZB = R / 32;
+  constexpr int KSW = COLS / 16;  // 16-column steps per wave
+  constexpr int PSTR = 33;       // padded row of a partial block (floats)
+  constexpr int ZROW = R + 8;    // padded token row of Z (bf16)
+  constexpr int NT = NW * 64;
+  __shared__ float red[NW * 32 * PSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t zt[32 * ZROW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qj = lane & 31, hh = lane >> 5;
+  const long tokens = (long)a.B * a.n;
+  const long tok = (long)blockIdx.x * 32 + qj;  // this lane's token
+  const bool tok_ok = tok < tokens;
+  const long tb = tok_ok ? tok / a.n : 0, ti = tok_ok ? tok % a.n : 0;
+  const int Hd = a.H * a.d;
+  auto optr = [&](int e) -> uint16_t* {
+    return a.out + ((tb * a.H + e / a.d) * a.n + ti) * a.d + e % a.d;
+  };
+  const int c0 = COLS * wave;
+
+  // ---- this wave's outputs, in the permuted k order (4 consecutive elements stay in one head)
+  u32x4 of[KSW];
+#pragma unroll
+  for (int s = 0; s < KSW; ++s) {
+    u32x2 lo = u32x2{0, 0}, hi = u32x2{0, 0};
+    if (tok_ok) {
+      lo = *reinterpret_cast<const u32x2*>(optr(c0 + 16 * s + 4 * hh));
+      hi = *reinterpret_cast<const u32x2*>(optr(c0 + 16 * s + 8 + 4 * hh));
+    }
+    of[s] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  // ---- partial Z^T over this wave's columns
+  f32x16 z[ZB];
+#pragma unroll
+  for (int zb = 0; zb < ZB; ++zb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[zb][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < KSW; ++s)
+#pragma unroll
+    for (int zb = 0; zb < ZB; ++zb) {
+      const uint16_t* wr = a.w_down + (long)(32 * zb + qj) * Hd + c0 + 16 * s + 4 * hh;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(wr);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(wr + 8);
+      z[zb] = mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, of[s], z[zb]);
+    }
+  // ---- Z^T = sum of the partials, one 32-row block at a time, stored as bf16 rows per token
+#pragma unroll
+  for (int zb = 0; zb < ZB; ++zb) {
+    float* mine = red + wave * 32 * PSTR;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * hh + (r & 3)) * PSTR + qj] = z[zb][r];
+    __syncthreads();
+    for (int e = tid; e < 32 * 32; e += NT) {
+      const int row = e & 31, t = e >> 5;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w * 32 * PSTR + row * PSTR + t];
+      zt[t * ZROW + 32 * zb + row] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+    __syncthreads();
+  }
+  // ---- G^T for this wave's rows, then the gate
+  u32x4 zf[R / 16];
+#pragma unroll
+  for (int s = 0; s < R / 16; ++s)
+    zf[s] = *reinterpret_cast<const u32x4*>(&zt[qj * ZROW + 16 * s + 8 * hh]);
+#pragma unroll
+  for (int b = 0; b < COLS / 32; ++b) {
+    const int ob = c0 + 32 * b;
+    f32x16 g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < R / 16; ++s) {
+      const u32x4 aw =
+          *reinterpret_cast<const u32x4*>(a.w_up + (long)(ob + qj) * R + 16 * s + 8 * hh);
+      g = mfma_32x32x16(aw, zf[s], g);
+    }
+    if (!tok_ok) continue;
+    // rows ob + 8q + 4hh + {0..3}: step 2b + q/2, slots 4(q%2) .. 4(q%2)+3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4& f = of[2 * b + (q >> 1)];
+      const uint32_t w0 = (q & 1) ? f[2] : f[0], w1 = (q & 1) ? f[3] : f[1];
+      u32x2 w;
+      w[0] = pack_bf16x2(bf16_lo(w0) * sigmoid_fast(g[4 * q]),
+                         bf16_hi(w0) * sigmoid_fast(g[4 * q + 1]));
+      w[1] = pack_bf16x2(bf16_lo(w1) * sigmoid_fast(g[4 * q + 2]),
+                         bf16_hi(w1) * sigmoid_fast(g[4 * q + 3]));
+      *reinterpret_cast<u32x2*>(optr(ob + 8 * q + 4 * hh)) = w;
+    }
+  }
+}
+
+template <int NW, int COLS>
+hipError_t launch_split(const GateArgs& a, long tokens, hipStream_t s) {
+  const dim3 grid((unsigned)((tokens + 31) / 32)), block(NW * 64);
+  switch (a.r) {
+    case 32: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 32, COLS>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 64, COLS>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 128, COLS>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
+#ifndef GATE_SPLIT_MAX
+#define GATE_SPLIT_MAX 1024
+#endif
 hipError_t launch_gate_lowrank(const GateArgs& a, hipStream_t s) {
   const long tokens = (long)a.B * a.n;
   if (tokens <= 0) return hipSuccess;
+  const int hd = a.H * a.d;
+  if (hd % 128 == 0 && hd <= GATE_SPLIT_MAX && a.r <= 128) {
+    switch (hd / 128) {
+      case 1: return launch_split<1, 128>(a, tokens, s);
+      case 2: return launch_split<2, 128>(a, tokens, s);
+      case 3: return launch_split<3, 128>(a, tokens, s);
+      case 4: return launch_split<4, 128>(a, tokens, s);
+      case 5: return launch_split<5, 128>(a, tokens, s);
+      case 6: return launch_split<6, 128>(a, tokens, s);
+      case 7: return launch_split<7, 128>(a, tokens, s);
+      case 8: return launch_split<8, 128>(a, tokens, s);
+      default: break;
+    }
+  }
   const dim3 grid((unsigned)((tokens + 127) / 128));
   switch (a.r) {
     case 32: hipLaunchKernelGGL(gate_lowrank_kernel<32>, grid, dim3(256), 0, s, a); break;

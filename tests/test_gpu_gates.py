@@ -82,9 +82,16 @@ def test_gated_forward_equals_gate_of_plain_forward_bits():
     assert (plain.view(torch.int16) == gated.view(torch.int16)).all()
 
 
+# H*d a multiple of 128 up to 1024 with r <= 128 takes the split kernel (one wave per 128
+# outputs: 1, 2, 3, 4, 6 and 8 waves below), the rest the general one (r = 256; H*d = 32, 480,
+# 1280 or 2048)
 @pytest.mark.parametrize("B,H,n,d,r", [(2, 12, 300, 64, 128), (1, 16, 1000, 64, 128),
                                        (1, 8, 50, 128, 32), (1, 4, 77, 64, 256),
-                                       (2, 2, 33, 16, 64)])
+                                       (2, 2, 33, 16, 64), (1, 2, 65, 128, 64),
+                                       (1, 8, 257, 64, 64), (2, 20, 40, 64, 32),
+                                       (1, 16, 300, 128, 128), (1, 6, 70, 80, 128),
+                                       (2, 2, 90, 64, 32), (1, 6, 100, 64, 64),
+                                       (1, 16, 16384, 64, 128)])
 def test_lowrank_gate(B, H, n, d, r):
     import torch
 
