@@ -77,8 +77,13 @@ struct STile {
   int ks0;       // window tiles: residue-subsequence index of row 0
 };
 
+// Occupancy: the dQ kind is held to 168 VGPRs at d = 64 (three waves per SIMD) and 256 at
+// d = 128 (two), where it would otherwise take a few more and lose a wave per SIMD (measured:
+// the dQ kernel 15% faster on dilated_16k, 35% on swa512_causal_32k, 5% slower on
+// longformer_base).  The dK/dV kind needs its registers (more of them spill).
 template <int D, int KIND, int NW, int MODE_MAIN>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
+    KIND == kBwdDQ ? (D == 64 ? 3 : 2) : 1))) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
   __shared__ BwdSmem<D> sm;
   const FwdCore a = args;
   const BwdArgs gp = gargs;
