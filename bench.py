@@ -511,6 +511,43 @@ def _gates_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _environment():
+    """The GPU, its clock and the software stack the numbers were taken with."""
+    import subprocess
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
+           "hbm_bytes": props.total_memory, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    env["max_sclk_mhz"] = None
+    try:  # the GPU agent's maximum engine clock, as rocminfo reports it
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30)
+        for agent in r.stdout.split("Agent ")[1:]:
+            if "Device Type:             GPU" in agent or "gfx9" in agent:
+                for ln in agent.splitlines():
+                    if "Max Clock Freq. (MHz)" in ln:
+                        env["max_sclk_mhz"] = int(ln.split(":")[1].split()[0])
+                        break
+                break
+    except (OSError, subprocess.SubprocessError, ValueError, IndexError):
+        pass
+    return env
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _source_hash():
     with open(MAIN_KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -562,6 +599,7 @@ def _cpu_baseline(inp, budget_gflop):
         "value": 4.0 * inp.d * E / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu": _cpu_model(),
         "kind": "oracle",
         "sample": f"heads {heads[0]}-{heads[-1]} of {inp.heads} (all rows), {E} entries, "
                   f"{4.0 * inp.d * E / 1e9:.1f} GFLOP fp64, {dt:.2f} s per pass, mean of {reps}",
@@ -729,6 +767,7 @@ def main():
         },
     }
     rec["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline(inp, args.cpu_budget_gflop)
+    rec["environment"] = _environment()
     del keep
     print(json.dumps(rec), flush=True)
 

@@ -15,7 +15,10 @@ def to_torch(inp, device):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
     def opt(a, dt):
-        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(device)
+        if a is None:
+            return None
+        h = np.ascontiguousarray(a, dtype=dt)
+        return torch.from_numpy(h if h.flags.writeable else h.copy()).to(device)
 
     return dict(
         q=mat(inp.q), k=mat(inp.k), v=mat(inp.v),
