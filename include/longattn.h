@@ -203,7 +203,7 @@ longattn_status longattn_backward_marked(const longattn_desc* desc, const void* 
  * radius <= 512, max_distance <= 512, num_buckets even in [4, 256], d_model a multiple of 64
  * and <= 4096 (the normalised global inputs are rounded to bf16 before the projections); other
  * valid values return LONGATTN_ERR_UNSUPPORTED.  Workspace: longattn_tglobal_workspace_size
- * bytes (covers both calls).
+ * bytes (covers both calls), 16-byte aligned (else LONGATTN_ERR_ALIGNMENT).
  * --------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch, heads, n, d;

@@ -27,7 +27,7 @@
 //
 // Data movement.  K and V tiles go from memory straight into LDS with 16-byte buffer loads (no
 // register staging; the buffer range check turns rows past the sequence end into zeros), two
-// stages each, one barrier per tile.  Half of the waves move K, the other half V.  K rows are
+// stages each, two barriers per tile.  Half of the waves move K, the other half V.  K rows are
 // read back as MFMA A operands with 16-byte reads; V stays row-major and its transposed A operand
 // is read with the transposing 64-bit LDS read.  Both layouts XOR-swizzle 16-byte chunks by row
 // so that the reads of a wave hit distinct banks.

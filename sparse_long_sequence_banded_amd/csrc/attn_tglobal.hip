@@ -21,8 +21,8 @@
 // The attention kernel is the forward kernel's scheme without dilation or layouts: a wave owns
 // 32 query rows (Q fragments in registers), 64-row K/V tiles (local keys, then global tokens)
 // stream through two LDS stages by direct buffer loads, S^T = K Q^T and O^T += V^T P^T on
-// 32x32x16 bf16 MFMA, and the softmax keeps a lazily moved per-row reference (weights stay below
-// 2^8 of it).
+// 32x32x16 bf16 MFMA, and the softmax keeps a lazily moved per-row reference (weights stay at
+// or below 2^16 of it).
 
 #include <type_traits>
 
@@ -36,6 +36,7 @@ using namespace mfma;
 
 constexpr float kLog2eT = 1.44269504088896340736f;
 constexpr float kRefSlack = 8.f;  // move a row's reference when its max exceeds it by > 2^8
+constexpr float kTgFastWeightSum = 65536.f;  // fast path: a lane's 16 weights of a half sum to <= 2^16
 
 // T5's bidirectional bucket of rel = key position - query position (fp64 decisions).
 __device__ int t5_bucket(int rel, int nb, int md) {
@@ -64,115 +65,138 @@ __global__ void tg_bias_kernel(TgArgs a, const float* tab_local, const float* ta
   }
 }
 
-// Block sums and RMS norm: y[b][g][c] (fp32 workspace) and side_valid[b][g].
-constexpr int kAggThreads = 256;
-__global__ __launch_bounds__(kAggThreads) void tg_aggregate_kernel(TgArgs a, const uint16_t* x,
-                                                                  const float* gamma,
-                                                                  uint16_t* y) {
-  __shared__ float red[kAggThreads / 64];
-  __shared__ int any_valid;
+// Block sums and RMS norm: y[b][g][c] (bf16) and side_valid[b][g].  One wave per (b, g); lane l
+// sums the 8-column groups l, l + 64, ... (KPG groups) over the block's rows with 16-byte loads,
+// ROWS rows at a time with every load in flight (a padded row is read and weighted by 0).
+template <int KPG>
+__global__ __launch_bounds__(64) void tg_aggregate_kernel(TgArgs a, const uint16_t* x,
+                                                         const float* gamma, uint16_t* y) {
+  constexpr int ROWS = KPG <= 2 ? 8 : (KPG == 4 ? 4 : 2);
   const int g = blockIdx.x % a.G;
   const int b = blockIdx.x / a.G;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const int i0 = g * a.blk;
   const int i1 = (g == a.G - 1) ? a.n : min(a.n, i0 + a.blk);  // the tail merges into the last
   const uint8_t* pad = a.kpad ? a.kpad + (long)b * a.n : nullptr;
-  if (t == 0) any_valid = 0;
-  __syncthreads();
-  float ss = 0.f;
-  int anyv = 0;
-  uint16_t* yrow = y + ((long)b * a.G + g) * a.dm;
-  // the sums stay in registers (model dims t, t + 256, ...) until the norm is known
-  constexpr int kPer = kTgMaxDm / kAggThreads;
-  float sums[kPer];
+  const int ng = a.dm / 8;
+  const uint16_t* xb = x + (long)b * a.n * a.dm;
+  float sum[KPG][8];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int c = t + kAggThreads * u;
-    float s = 0.f;
-    if (c < a.dm) {
-      for (int i = i0; i < i1; ++i) {
-        if (pad && pad[i]) continue;
-        s += __uint_as_float((uint32_t)x[((long)b * a.n + i) * a.dm + c] << 16);
+  for (int u = 0; u < KPG; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[u][e] = 0.f;
+  bool anyv = false;
+  for (int i = i0; i < i1; i += ROWS) {
+    u32x4 xv[ROWS][KPG];
+    float wt[ROWS];
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+      const int row = min(i + k, i1 - 1);
+      wt[k] = (i + k < i1 && (pad == nullptr || pad[row] == 0)) ? 1.f : 0.f;
+#pragma unroll
+      for (int u = 0; u < KPG; ++u) {
+        const int cg = lane + 64 * u;
+        xv[k][u] = cg < ng ? *reinterpret_cast<const u32x4*>(xb + (long)row * a.dm + 8 * cg)
+                           : u32x4{0, 0, 0, 0};
       }
     }
-    sums[u] = s;
-    ss = __builtin_fmaf(s, s, ss);
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+      anyv = anyv || wt[k] != 0.f;
+#pragma unroll
+      for (int u = 0; u < KPG; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[u][2 * e] = __builtin_fmaf(wt[k], bf16_lo(xv[k][u][e]), sum[u][2 * e]);
+          sum[u][2 * e + 1] = __builtin_fmaf(wt[k], bf16_hi(xv[k][u][e]), sum[u][2 * e + 1]);
+        }
+    }
   }
-  for (int i = i0 + t; i < i1; i += kAggThreads) anyv |= (pad == nullptr || pad[i] == 0);
-  if (anyv) any_valid = 1;  // benign race: every writer stores 1
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < KPG; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(sum[u][e], sum[u][e], ss);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((t & 63) == 0) red[t >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
+  const float inv = 1.f / sqrtf(ss / (float)a.dm + a.eps);
+  uint16_t* yrow = y + ((long)b * a.G + g) * a.dm;
 #pragma unroll
-  for (int w = 0; w < kAggThreads / 64; ++w) tot += red[w];
-  const float inv = 1.f / sqrtf(tot / (float)a.dm + a.eps);
+  for (int u = 0; u < KPG; ++u) {
+    const int cg = lane + 64 * u;
+    if (cg >= ng) continue;
+    u32x4 w;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int c = t + kAggThreads * u;
-    if (c < a.dm) yrow[c] = __builtin_bit_cast(uint16_t, (__bf16)(sums[u] * inv * gamma[c]));
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack_bf16x2(sum[u][2 * e] * inv * gamma[8 * cg + 2 * e],
+                         sum[u][2 * e + 1] * inv * gamma[8 * cg + 2 * e + 1]);
+    *reinterpret_cast<u32x4*>(yrow + 8 * cg) = w;
   }
-  if (t == 0) a.side_valid[(long)b * a.G + g] = (uint8_t)any_valid;
+  // the valid flag is the same in every lane (the row weights are uniform)
+  if (lane == 0) a.side_valid[(long)b * a.G + g] = (uint8_t)anyv;
 }
 
 // side_k / side_v [B][H][G][d] (bf16) = y [B*G][dm] (bf16) times W [dm][H*d] (bf16), on
-// 32x32x16 bf16 MFMA with fp32 sums.  A workgroup of 4 waves makes a 64 x 64 output tile of one
-// matrix (2 x 2 waves of 32 x 32); per 64-deep k chunk the W tile (64 x 64) goes to LDS and each
-// wave reads its B operands with the transposing LDS read.  The MFMA's k slots of lane half hh
-// are k = 4hh + {0..3} and 8 + 4hh + {0..3} within each 16-deep step (the transposing read's
-// order), and the A operands (y rows, read from memory) follow the same order.
-constexpr int kProjTile = 64, kProjK = 64;
-__global__ __launch_bounds__(256) void tg_project_kernel(TgArgs a, const uint16_t* y,
-                                                        const uint16_t* wk,
-                                                        const uint16_t* wv) {
-  __shared__ __attribute__((aligned(16))) uint16_t ws[kProjK][kProjTile];  // W[k][col] tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// 32x32x16 bf16 MFMA with fp32 sums.  One wave makes a 32 x 32 output tile of one matrix.  Per
+// 256-deep k chunk the W tile (256 x 32) and the y tile (32 x 256) go straight to LDS with
+// 16-byte buffer loads (no register staging, every load in flight); the wave then reads its B
+// operands with the transposing LDS read and its A operands with 8-byte LDS reads.  The y tile's
+// 16-byte chunk c of row r sits at position c ^ r of the row, so the 32 rows' reads of one chunk
+// hit different banks.  The MFMA's k slots of lane half hh are k = 4hh + {0..3} and
+// 8 + 4hh + {0..3} within each 16-deep step (the transposing read's order), and the A operands
+// follow the same order.
+constexpr int kProjTile = 32, kProjK = 256;
+__global__ __launch_bounds__(64) void tg_project_kernel(TgArgs a, const uint16_t* y,
+                                                       const uint16_t* wk, const uint16_t* wv) {
+  constexpr int KSC = kProjK / 16;  // k-steps per chunk
+  __shared__ __attribute__((aligned(1024))) uint16_t ws[kProjK][kProjTile];  // W[k][col] chunk
+  __shared__ __attribute__((aligned(1024))) uint16_t ys[kProjTile][kProjK];  // y[row][k] chunk
+  const int lane = threadIdx.x;
   const int qj = lane & 31, hh = lane >> 5;
   const long rows = (long)a.B * a.G;
   const int HD = a.H * a.D;
-  const long r0 = (long)blockIdx.x * kProjTile + 32 * (wave >> 1);  // this wave's rows
+  const long r0 = (long)blockIdx.x * kProjTile;
   const int c0 = blockIdx.y * kProjTile;
-  const int wc = 32 * (wave & 1);  // this wave's columns within the tile
   const bool is_v = blockIdx.z == 1;
-  const uint16_t* W = is_v ? wv : wk;
-  const long arow = r0 + qj;  // A row of this lane
-  const uint16_t* yr = y + (arow < rows ? arow : 0) * a.dm;
+  // W rows are read from column c0 on, y rows from row r0 on; out-of-range reads give zeros
+  const u32x4 wrs = buf_rsrc((is_v ? wv : wk) + c0,
+                             (uint32_t)(((long)a.dm * HD - c0) * 2));
+  const u32x4 yrs = buf_rsrc(y + r0 * a.dm, (uint32_t)((rows - r0) * a.dm * 2));
+  const uint32_t ws_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ws[0][0]));
+  const uint32_t ys_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ys[0][0]));
+  const int vi = lane & 15, vg = lane >> 4;
+  const int trow = 4 * hh + (vi >> 2);
+  const int tcol = 16 * (vg & 1) + 4 * (vi & 3);
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   for (int k0 = 0; k0 < a.dm; k0 += kProjK) {
-    __syncthreads();
-    // stage W[k0 .. k0+63][c0 .. c0+63]: 256 threads x 32 bytes
-    {
-      const int row = tid >> 2, part = tid & 3;
-      const int col = c0 + 16 * part;
-      u32x4 v0 = u32x4{0, 0, 0, 0}, v1 = u32x4{0, 0, 0, 0};
-      if (col < HD) {
-        const uint16_t* src = W + (long)(k0 + row) * HD + col;
-        v0 = *reinterpret_cast<const u32x4*>(src);
-        v1 = *reinterpret_cast<const u32x4*>(src + 8);
-      }
-      *reinterpret_cast<u32x4*>(&ws[row][16 * part]) = v0;
-      *reinterpret_cast<u32x4*>(&ws[row][16 * part + 8]) = v1;
+    const int kc = min(kProjK, a.dm - k0);  // a multiple of 64
+    if (k0 > 0) __syncthreads();  // the previous chunk is consumed
+    // W: 16 rows of 64 bytes per load (lane l: row 16i + l/4, columns 8(l%4) .. + 7)
+    for (int i = 0; i < kc / 16; ++i)
+      lds_dma16(wrs, (uint32_t)(((k0 + 16 * i + (lane >> 2)) * HD + 8 * (lane & 3)) * 2),
+                ws_lds + 1024 * i);
+    // y: two rows per load; lane l fills position l%32 of row 2j + l/32 with that row's chunk
+    // (l%32) ^ row (chunks past kc hold data that is never read)
+    for (int j = 0; j < kProjTile / 2; ++j) {
+      const int row = 2 * j + (lane >> 5);
+      const int chunk = (lane & 31) ^ row;
+      lds_dma16(yrs, (uint32_t)((row * a.dm + k0 + 8 * chunk) * 2), ys_lds + 1024 * j);
     }
+    wait_vmcnt<0>();
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kProjK / 16; ++ks) {
-      const int kb = k0 + 16 * ks;
-      // A: y[arow][kb + 4hh + {0..3}] and y[arow][kb + 8 + 4hh + {0..3}]
-      u32x2 lo = u32x2{0, 0}, hi = u32x2{0, 0};
-      if (arow < rows) {
-        lo = *reinterpret_cast<const u32x2*>(yr + kb + 4 * hh);
-        hi = *reinterpret_cast<const u32x2*>(yr + kb + 8 + 4 * hh);
-      }
-      // B: W[kb + 4hh + e][col] and W[kb + 8 + 4hh + e][col] for col = wc + qj, by the
-      // transposing read (lane l of 16-lane group G = l/16 names row 4*(l/32) + (l%16)/4 of
-      // the 4-row group and 4 columns)
-      const int vi = lane & 15, vg = lane >> 4;
+    for (int ks = 0; ks < KSC; ++ks) {
+      if (16 * ks >= kc) break;
+      // A: y[row qj][16ks + 4hh + {0..3}] (chunk 2ks) and y[row qj][16ks + 8 + 4hh + {0..3}]
+      // (chunk 2ks + 1), the (8hh)-th bytes of those chunks
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(&ys[qj][8 * ((2 * ks) ^ qj) + 4 * hh]);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(&ys[qj][8 * ((2 * ks + 1) ^ qj) + 4 * hh]);
+      // B: W[kb + 4hh + e][col] and W[kb + 8 + 4hh + e][col] for col = qj, by the transposing
+      // read (lane l of 16-lane group G = l/16 names row 4*(l/32) + (l%16)/4 of the 4-row group
+      // and 4 columns)
       const unsigned char* base = reinterpret_cast<const unsigned char*>(&ws[16 * ks][0]);
-      const int trow = 4 * hh + (vi >> 2);
-      const int tcol = wc + 16 * (vg & 1) + 4 * (vi & 3);
       const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           LDS_PTR(s16x4, base + trow * (2 * kProjTile) + 2 * tcol));
       const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -182,8 +206,8 @@ __global__ __launch_bounds__(256) void tg_project_kernel(TgArgs a, const uint16_
                           acc);
     }
   }
-  // C: lane (col qj, hh) holds rows 8(r/4) + 4hh + r%4 of the wave's 32 x 32 block
-  const int col = c0 + wc + qj;
+  // C: lane (col qj, hh) holds rows 8(r/4) + 4hh + r%4 of the 32 x 32 tile
+  const int col = c0 + qj;
   if (col >= HD) return;
   const int h = col / a.D, c = col % a.D;
   uint16_t* dst = is_v ? a.sv_out : a.sk_out;
@@ -337,7 +361,12 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
         sc[kb] = mfma_32x32x16(kf, qf[ks], sc[kb]);
       }
     }
-    // scores in log2 units plus bias; register r of half kb is row 32kb + 8(r/4) + 4hh + r%4
+    // Scores in log2 units plus bias, x = mul * y + off; register r of half kb is row
+    // 32kb + 8(r/4) + 4hh + r%4.  Local tiles and near global-token tiles take a bias per element
+    // (y = c2 s + bias, mul = 1, off = 0); a global-token tile whose distances to all of the
+    // wave's blocks are saturated takes one constant, folded into the exponent (y = s, mul = c2,
+    // off = that bias).
+    float mul = 1.f, off = 0.f;
     if (local) {
       // bias_l index: (base + row) - qpos + rl, a per-lane base plus a constant per register
       const float* bl = sm.bias_l + (base - qpos + a.rl + 4 * hh);
@@ -350,11 +379,8 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
       const int far_pos = base - wblk_hi >= a.md;                  // every g - block >= md
       const int far_neg = base + kKeyTile - 1 - wblk_lo <= -a.md;  // every g - block <= -md
       if (far_pos || far_neg) {
-        const float bc = far_pos ? sm.bias_s[2 * a.md] : sm.bias_s[0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[kb][r] = __builtin_fmaf(sc[kb][r], c2, bc);
+        mul = c2;
+        off = far_pos ? sm.bias_s[2 * a.md] : sm.bias_s[0];
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -366,8 +392,12 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
           }
       }
     }
-    // masks: usable rows, and for local tiles the window |key - q| <= radius
-    {
+    // masks (usable rows, and for local tiles the window |key - q| <= radius), only where some
+    // key of the tile is excluded for some row of the wave
+    bool need_mask = vmask != ~0ull || w_first + RW > a.n;
+    if (local && !need_mask)
+      need_mask = !(base >= w_last - a.radius && base + kKeyTile - 1 <= w_first + a.radius);
+    if (need_mask) {
       unsigned long long m = vmask >> (4 * hh);
       if (local) {
         const int lo = qpos - a.radius - base - 4 * hh;
@@ -388,39 +418,56 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
         for (int r = 0; r < 16; ++r) sc[kb][r] = keep_if_bit(sc[kb][r], w, 8 * (r >> 2) + (r & 3), ninf);
       }
     }
-    // online softmax per 32-key half, lazy reference, then O^T += V^T P^T
+    // Online softmax per 32-key half against the row's reference ref: weights 2^(x - ref).
+    // Fast path: exponentiate without a row max and accept when every lane's 16 weights sum to
+    // at most 2^16 (no weight above 2^16, nothing overflows).  Otherwise (a row's first allowed
+    // key, or a score far above ref) take the half's row max; a row moves ref to it when it has
+    // none yet or when the max exceeds ref by more than 2^8, and the weights are redone.  Then
+    // O^T += V^T P^T.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16& u = sc[kb];
-      float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
-      float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
-      x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
-      x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), __builtin_fmaxf(x1, u[15]));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
-                                                       false, false);
-      const float xm = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const bool need = (xm != ninf) & (!has | (xm - ref > kRefSlack));
-      if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-        const float nref = need ? xm : ref;
-        const float alpha = has ? exp2_fast(ref - nref) : 1.f;
-        ref = nref;
-        has = has || need;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
       uint32_t pk[8];
       float part = 0.f;
+      auto exponentiate = [&]() {
+        const float add = off - ref;
+        float la = 0.f, lb = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(u[r] - ref), p1 = exp2_fast(u[r + 1] - ref);
-        pk[r >> 1] = pack_bf16x2(p0, p1);
-        part += p0 + p1;
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(__builtin_fmaf(u[r], mul, add));
+          const float p1 = exp2_fast(__builtin_fmaf(u[r + 1], mul, add));
+          pk[r >> 1] = pack_bf16x2(p0, p1);
+          la += p0;
+          lb += p1;
+        }
+        part = la + lb;
+      };
+      exponentiate();
+      if (__builtin_amdgcn_ballot_w64(!has | !(part <= kTgFastWeightSum)) != 0ull) {
+        float x0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
+        float x1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[6]), u[7]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[8]), u[9]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[10]), u[11]);
+        x1 = __builtin_fmaxf(__builtin_fmaxf(x1, u[12]), u[13]);
+        x0 = __builtin_fmaxf(__builtin_fmaxf(x0, u[14]), __builtin_fmaxf(x1, u[15]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0),
+                                                         false, false);
+        const float xm = __builtin_fmaf(
+            __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), mul, off);
+        const bool need = (xm != ninf) & (!has | (xm - ref > kRefSlack));
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+          const float nref = need ? xm : ref;
+          const float alpha = has ? exp2_fast(ref - nref) : 1.f;
+          ref = nref;
+          has = has || need;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        exponentiate();
       }
       l_run += part;
 #pragma unroll
@@ -484,12 +531,16 @@ hipError_t launch_tglobal_side(const TgArgs& a, const uint16_t* x, const float* 
                                const uint16_t* wk, const uint16_t* wv, uint16_t* y,
                                hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(tg_aggregate_kernel, dim3((unsigned)(a.B * a.G)), dim3(kAggThreads), 0, s,
-                     a, x, gamma, y);
+  const dim3 agrid((unsigned)(a.B * a.G));
+  const int groups = a.dm / 8;  // 8-column groups of a row
+  if (groups <= 64) hipLaunchKernelGGL(tg_aggregate_kernel<1>, agrid, dim3(64), 0, s, a, x, gamma, y);
+  else if (groups <= 128) hipLaunchKernelGGL(tg_aggregate_kernel<2>, agrid, dim3(64), 0, s, a, x, gamma, y);
+  else if (groups <= 256) hipLaunchKernelGGL(tg_aggregate_kernel<4>, agrid, dim3(64), 0, s, a, x, gamma, y);
+  else hipLaunchKernelGGL(tg_aggregate_kernel<8>, agrid, dim3(64), 0, s, a, x, gamma, y);
   const long rows = (long)a.B * a.G;
   const dim3 grid((unsigned)((rows + kProjTile - 1) / kProjTile),
                   (unsigned)((a.H * a.D + kProjTile - 1) / kProjTile), 2);
-  hipLaunchKernelGGL(tg_project_kernel, grid, dim3(256), 0, s, a, y, wk, wv);
+  hipLaunchKernelGGL(tg_project_kernel, grid, dim3(64), 0, s, a, y, wk, wv);
   return hipGetLastError();
 }
 

@@ -612,6 +612,7 @@ longattn_status longattn_tglobal_side(const longattn_tglobal_desc* desc, const v
     if (!aligned16(t)) return LONGATTN_ERR_ALIGNMENT;
   if ((reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LONGATTN_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LONGATTN_ERR_ALIGNMENT;  // rows of normalised inputs
   TgArgs& a = p.a;
   a.side_valid = side_valid;
   a.sk_out = static_cast<uint16_t*>(side_k);
@@ -638,6 +639,7 @@ longattn_status longattn_tglobal_forward(const longattn_tglobal_desc* desc, cons
   for (const void* t : {q, k, v, side_k, side_v, static_cast<const void*>(out)})
     if (!aligned16(t)) return LONGATTN_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes < p.ws_bytes) return LONGATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LONGATTN_ERR_ALIGNMENT;
   TgArgs& a = p.a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

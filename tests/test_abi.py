@@ -351,6 +351,11 @@ def test_tglobal_workspace_covers_both_calls():
         la.LONGATTN_ERR_WORKSPACE
     assert la.longattn_tglobal_forward(d, FAKE + 2, *([FAKE] * 9), FAKE, 1 << 30, None) == \
         la.LONGATTN_ERR_ALIGNMENT
+    # the workspace itself must be 16-byte aligned
+    assert la.longattn_tglobal_side(d, *([FAKE] * 7), FAKE + 4, 1 << 30, None) == \
+        la.LONGATTN_ERR_ALIGNMENT
+    assert la.longattn_tglobal_forward(d, *([FAKE] * 10), FAKE + 8, 1 << 30, None) == \
+        la.LONGATTN_ERR_ALIGNMENT
     assert la.longattn_tglobal_side(_tdesc(batch=0), *([None] * 7), None, 0, None) == \
         la.LONGATTN_OK
 
