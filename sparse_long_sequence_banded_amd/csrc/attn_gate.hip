@@ -134,11 +134,13 @@ __global__ __launch_bounds__(256) void gate_lowrank_kernel(GateArgs a) {
 //   Z^T: wave w multiplies its 256 columns of W_down with its outputs (a split of the sum over
 //   H*d), and the NW partial sums are added through LDS, one 32-row block of Z^T at a time.
 //   G^T: wave w computes its 256 rows, then gates its own outputs.
-// The order of the sum in the first product is free, so a lane's eight k-slots of 16-column step
-// s are taken as columns 16s + 4hh + {0..3} and 16s + 8 + 4hh + {0..3} (for A and B alike):
-// these are exactly the elements the accumulator layout of the second product puts in that lane
-// (rows 8q + 4hh + {0..3} of a 32-row block), so the outputs stay in registers between the two
-// products and are read from memory once.
+// In the first product a lane's eight k-slots of 16-column step s are the columns
+// 16s + 8hh + {0..7} (one 16-byte load each of outputs and of W_down).  In the second product
+// the order of the output rows within a 32-row block is free: A's row qj = 8q + 4h' + e is taken
+// as W_up row pi(qj) = 16(q/2) + 8h' + 4(q%2) + e, so lane half hh's accumulators hold rows
+// 16(q/2) + 8hh + 4(q%2) + {0..3}: exactly the columns that lane loaded in steps 2b and 2b + 1.
+// The outputs therefore stay in registers between the two products and are read from memory
+// once.
 template <int NW, int R, int COLS>
 __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a) {
   constexpr int ZB = R / 32;
@@ -161,16 +163,13 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
   };
   const int c0 = COLS * wave;
 
-  // ---- this wave's outputs, in the permuted k order (4 consecutive elements stay in one head)
+  // ---- this wave's outputs: columns 16s + 8hh + {0..7} (8 consecutive elements stay in one
+  // head: d is a multiple of 16)
   u32x4 of[KSW];
 #pragma unroll
   for (int s = 0; s < KSW; ++s) {
-    u32x2 lo = u32x2{0, 0}, hi = u32x2{0, 0};
-    if (tok_ok) {
-      lo = *reinterpret_cast<const u32x2*>(optr(c0 + 16 * s + 4 * hh));
-      hi = *reinterpret_cast<const u32x2*>(optr(c0 + 16 * s + 8 + 4 * hh));
-    }
-    of[s] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    of[s] = u32x4{0, 0, 0, 0};
+    if (tok_ok) of[s] = *reinterpret_cast<const u32x4*>(optr(c0 + 16 * s + 8 * hh));
   }
   // ---- partial Z^T over this wave's columns
   f32x16 z[ZB];
@@ -182,10 +181,9 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
   for (int s = 0; s < KSW; ++s)
 #pragma unroll
     for (int zb = 0; zb < ZB; ++zb) {
-      const uint16_t* wr = a.w_down + (long)(32 * zb + qj) * Hd + c0 + 16 * s + 4 * hh;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(wr);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(wr + 8);
-      z[zb] = mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, of[s], z[zb]);
+      const u32x4 aw = *reinterpret_cast<const u32x4*>(a.w_down + (long)(32 * zb + qj) * Hd +
+                                                       c0 + 16 * s + 8 * hh);
+      z[zb] = mfma_32x32x16(aw, of[s], z[zb]);
     }
   // ---- Z^T = sum of the partials, one 32-row block at a time, stored as bf16 rows per token
 #pragma unroll
@@ -203,7 +201,8 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
     }
     __syncthreads();
   }
-  // ---- G^T for this wave's rows, then the gate
+  // ---- G^T for this wave's rows (A row qj is W_up row pi(qj) of the block), then the gate
+  const int prow = 16 * (qj >> 4) + 8 * ((qj >> 2) & 1) + 4 * ((qj >> 3) & 1) + (qj & 3);
   u32x4 zf[R / 16];
 #pragma unroll
   for (int s = 0; s < R / 16; ++s)
@@ -217,11 +216,12 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
 #pragma unroll
     for (int s = 0; s < R / 16; ++s) {
       const u32x4 aw =
-          *reinterpret_cast<const u32x4*>(a.w_up + (long)(ob + qj) * R + 16 * s + 8 * hh);
+          *reinterpret_cast<const u32x4*>(a.w_up + (long)(ob + prow) * R + 16 * s + 8 * hh);
       g = mfma_32x32x16(aw, zf[s], g);
     }
     if (!tok_ok) continue;
-    // rows ob + 8q + 4hh + {0..3}: step 2b + q/2, slots 4(q%2) .. 4(q%2)+3
+    // registers 4q .. 4q+3: rows ob + 16(q/2) + 8hh + 4(q%2) + {0..3}, i.e. step 2b + q/2,
+    // slots 4(q%2) .. 4(q%2)+3
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const u32x4& f = of[2 * b + (q >> 1)];
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
                          bf16_hi(w0) * sigmoid_fast(g[4 * q + 1]));
       w[1] = pack_bf16x2(bf16_lo(w1) * sigmoid_fast(g[4 * q + 2]),
                          bf16_hi(w1) * sigmoid_fast(g[4 * q + 3]));
-      *reinterpret_cast<u32x2*>(optr(ob + 8 * q + 4 * hh)) = w;
+      *reinterpret_cast<u32x2*>(optr(ob + 16 * (q >> 1) + 8 * hh + 4 * (q & 1))) = w;
     }
   }
 }
