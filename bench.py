@@ -27,7 +27,6 @@ METRIC = "useful TFLOP/s + % bf16 MFMA peak, window attn fwd at n=4096/16384 (1 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 DEFAULT_WORKLOAD = "dilated_16k"
-MAIN_KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", "attn_mfma.hip")
 
 
 def _parse():
@@ -548,23 +547,23 @@ def _cpu_model():
     return None
 
 
-def _source_hash():
-    with open(MAIN_KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def _traffic_of(profile, source):
     """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE scaled by a copy kernel's readings), if it was taken on the current kernel
-    source (else None)."""
+    sources (the summary lists them, `source` first; their joint hash must match), else None."""
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", source), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != digest:
+    sources = rec.get("sources") or [source]
+    if sources[0] != source:
+        return None
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(ROOT, "sparse_long_sequence_banded_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if rec.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
         return None
     return rec.get("hbm_bytes_per_launch")
 

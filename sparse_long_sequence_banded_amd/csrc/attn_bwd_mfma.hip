@@ -78,9 +78,10 @@ struct STile {
 };
 
 // Occupancy: the dQ kind is held to 168 VGPRs at d = 64 (three waves per SIMD) and 256 at
-// d = 128 (two), where it would otherwise take a few more and lose a wave per SIMD (measured:
-// the dQ kernel 15% faster on dilated_16k, 35% on swa512_causal_32k, 5% slower on
-// longformer_base).  The dK/dV kind needs its registers (more of them spill).
+// d = 128 (two); one wave per SIMD more than a few extra registers would leave (measured: the dQ
+// kernel 15% faster on dilated_16k, 35% on swa512_causal_32k).  Working on the streamed tile in
+// 32-row halves keeps it within those bounds without spilling.  The dK/dV kind needs its
+// registers (capping it spills).
 template <int D, int KIND, int NW, int MODE_MAIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     KIND == kBwdDQ ? (D == 64 ? 3 : 2) : 1))) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
@@ -539,55 +540,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     auto compute = [&](int si, const STile& T, unsigned long long vmask, bool need_band) {
       const unsigned char* sa = sm.stage_a[si];
       const unsigned char* sb = sm.stage_b[si];
-      // raw scores and dP, both C[streamed][owner]
-      f32x16 sc[2], dp[2];
+      // per 32-row half kb of the streamed tile: raw scores and dP (both C[streamed][owner]),
+      // masks, P and dS, and the accumulation
+      const bool masked = need_band || vmask != ~0ull ||
+                          (!DQ && __builtin_amdgcn_ballot_w64(!own_ok) != 0ull);
+      unsigned long long m = vmask >> (4 * hh);
+      if (need_band) {
+        const int lo = osub - WL - T.ks0 - 4 * hh;
+        const int hi = osub + WR - T.ks0 - 4 * hh;
+        unsigned long long bm = 0ull;
+        if (hi >= 0 && lo <= 63) {
+          const int lc = max(lo, 0), hc = min(hi, 63);
+          bm = (~0ull >> (63 - (hc - lc))) << lc;
+        }
+        m &= bm;
+      }
+      if (!own_ok && !DQ) m = 0ull;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sc[kb][r] = 0.f;
-          dp[kb][r] = 0.f;
+          sc[r] = 0.f;
+          dp[r] = 0.f;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 xa = *reinterpret_cast<const u32x4*>(sa + koa[ks] + kb * 32 * (2 * D));
-          sc[kb] = mfma_32x32x16(xa, fa[ks], sc[kb]);
+          sc = mfma_32x32x16(xa, fa[ks], sc);
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 xb = *reinterpret_cast<const u32x4*>(sb + kob[ks] + kb * 32 * (2 * D));
-          dp[kb] = mfma_32x32x16(xb, fb[ks], dp[kb]);
+          dp = mfma_32x32x16(xb, fb[ks], dp);
         }
-      }
-      // masks: register r of block kb is streamed row 32kb + 8(r/4) + 4hh + r%4
-      {
-        unsigned long long m = vmask >> (4 * hh);
-        if (need_band) {
-          const int lo = osub - WL - T.ks0 - 4 * hh;
-          const int hi = osub + WR - T.ks0 - 4 * hh;
-          unsigned long long bm = 0ull;
-          if (hi >= 0 && lo <= 63) {
-            const int lc = max(lo, 0), hc = min(hi, 63);
-            bm = (~0ull >> (63 - (hc - lc))) << lc;
-          }
-          m &= bm;
-        }
-        if (!own_ok && !DQ) m = 0ull;
-        if (need_band || vmask != ~0ull || (!DQ && __builtin_amdgcn_ballot_w64(!own_ok) != 0ull)) {
+        if (masked) {
           const float ninf = neg_inf();
+          uint32_t w = (uint32_t)(m >> (32 * kb));
+          asm("" : "+v"(w));
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            uint32_t w = (uint32_t)(m >> (32 * kb));
-            asm("" : "+v"(w));
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              sc[kb][r] = keep_if_bit(sc[kb][r], w, 8 * (r >> 2) + (r & 3), ninf);
-          }
+          for (int r = 0; r < 16; ++r) sc[r] = keep_if_bit(sc[r], w, 8 * (r >> 2) + (r & 3), ninf);
         }
-      }
-      // P = 2^(c2 s - lse2), dS = P (dP - Drow); packed to bf16 as B operands
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
         uint32_t pk[8], dk[8];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -609,8 +602,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
-            pe[e] = exp2_fast(__builtin_fmaf(sc[kb][r], c2, -l4[e]));
-            de[e] = pe[e] * (dp[kb][r] - d4[e]);
+            pe[e] = exp2_fast(__builtin_fmaf(sc[r], c2, -l4[e]));
+            de[e] = pe[e] * (dp[r] - d4[e]);
           }
           pk[2 * q4] = pack_bf16x2(pe[0], pe[1]);
           pk[2 * q4 + 1] = pack_bf16x2(pe[2], pe[3]);

@@ -41,12 +41,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // s if bit `bit` of w is set, else ninf (which holds -inf): a sign-extended one-bit field
-// extract and a bitfield select.
+// extract and a bitfield select (the and/or form below compiles to v_bfi_b32).  Plain code, not
+// inline assembly: s is often a matrix-core result, and only instructions the compiler sees get
+// the wait states a vector read of such a result needs.
 __device__ __forceinline__ float keep_if_bit(float s, uint32_t w, int bit, float ninf) {
-  const int sel = __builtin_amdgcn_sbfe((int)w, bit, 1);
-  float r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(sel), "v"(s), "v"(ninf));
-  return r;
+  const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)w, bit, 1);
+  return __uint_as_float((sel & __float_as_uint(s)) | (~sel & __float_as_uint(ninf)));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
