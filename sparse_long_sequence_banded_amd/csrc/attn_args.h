@@ -55,7 +55,8 @@ struct BwdArgs {
   float* drow;       // [B][H][n] workspace: dO . O per row
   float* lse2;       // [B][H][n] workspace: lse in log2 units (matrix-core path)
 };
-enum BwdKind : int { kBwdDQ = 0, kBwdDKV = 1 };
+// dQ; dK and dV together; or dK and dV in two passes (each recomputes the scores)
+enum BwdKind : int { kBwdDQ = 0, kBwdDKV = 1, kBwdDK = 2, kBwdDV = 3 };
 
 // Sliding-window decode over a key/value cache.
 constexpr int kDecodeGenericChunk = 256;  // cache positions per workgroup, generic head dims

@@ -46,6 +46,13 @@
 #include "attn_args.h"
 #include "mfma_util.h"
 
+#ifndef BWD_DV_WAVES_128
+#define BWD_DV_WAVES_128 2
+#endif
+#ifndef BWD_SPLIT_DKV_MASK
+#define BWD_SPLIT_DKV_MASK 2  // bit 0: d = 64, bit 1: d = 128
+#endif
+
 namespace longattn {
 namespace {
 
@@ -84,7 +91,9 @@ struct STile {
 // registers (capping it spills).
 template <int D, int KIND, int NW, int MODE_MAIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
-    KIND == kBwdDQ ? (D == 64 ? 3 : 2) : 1))) void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
+    (KIND == kBwdDQ || KIND == kBwdDK) ? (D == 64 ? 3 : 2)
+                                       : (KIND == kBwdDV ? (D == 64 ? 4 : BWD_DV_WAVES_128) : 1))))
+void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
   __shared__ BwdSmem<D> sm;
   const FwdCore a = args;
   const BwdArgs gp = gargs;
@@ -120,6 +129,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   auto body = [&](auto mode_c, const int wg) {
     constexpr int MODE = decltype(mode_c)::value;
     constexpr bool DQ = KIND == kBwdDQ;
+    constexpr bool ACC0 = KIND != kBwdDV;                       // dQ^T or dK^T
+    constexpr bool ACC1 = KIND == kBwdDKV || KIND == kBwdDV;    // dV^T
+    constexpr bool NEED_DP = KIND != kBwdDV;                    // dP (for dS)
     constexpr int NT = NW * 64, RW = 32, QT = NW * RW;
     constexpr int CH = D / 8;          // 16-byte chunks per row
     constexpr int KS = D / 16;         // MFMA k-steps over the head dim
@@ -339,7 +351,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       fb[s] = u32x4{0, 0, 0, 0};
       if (opos >= 0) {
         fa[s] = *reinterpret_cast<const u32x4*>(OA + (long)opos * D + 16 * s + 8 * hh);
-        fb[s] = *reinterpret_cast<const u32x4*>(OB + (long)opos * D + 16 * s + 8 * hh);
+        if (NEED_DP || DQ)
+          fb[s] = *reinterpret_cast<const u32x4*>(OB + (long)opos * D + 16 * s + 8 * hh);
       }
     }
     // dQ: the owner query's lse2 (lse in log2 units; 0 for an empty row, whose edges are all
@@ -443,7 +456,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       }
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(fa[s]), "v"(fb[s]));
+    for (int s = 0; s < KS; ++s) {
+      asm volatile("" : : "v"(fa[s]));
+      if constexpr (NEED_DP) asm volatile("" : : "v"(fb[s]));
+    }
     __syncthreads();
     if (n_local == 0 && n_tiles > 0) issue(0, tile_of(0));
 
@@ -569,10 +585,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 xa = *reinterpret_cast<const u32x4*>(sa + koa[ks] + kb * 32 * (2 * D));
           sc = mfma_32x32x16(xa, fa[ks], sc);
         }
+        if constexpr (NEED_DP) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 xb = *reinterpret_cast<const u32x4*>(sb + kob[ks] + kb * 32 * (2 * D));
-          dp = mfma_32x32x16(xb, fb[ks], dp);
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 xb = *reinterpret_cast<const u32x4*>(sb + kob[ks] + kb * 32 * (2 * D));
+            dp = mfma_32x32x16(xb, fb[ks], dp);
+          }
         }
         if (masked) {
           const float ninf = neg_inf();
@@ -618,8 +636,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const u32x4 bp = {pk[4 * gh], pk[4 * gh + 1], pk[4 * gh + 2], pk[4 * gh + 3]};
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            acc0[db] = mfma_32x32x16(read_t(sa, grp, db), bds, acc0[db]);  // dQ^T or dK^T
-            if constexpr (!DQ) acc1[db] = mfma_32x32x16(read_t(sb, grp, db), bp, acc1[db]);
+            if constexpr (ACC0) acc0[db] = mfma_32x32x16(read_t(sa, grp, db), bds, acc0[db]);
+            if constexpr (ACC1) acc1[db] = mfma_32x32x16(read_t(sb, grp, db), bp, acc1[db]);
           }
         }
       }
@@ -674,10 +692,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int d = 32 * db + 8 * rq + 4 * hh;
-          *reinterpret_cast<float4*>(po + d) =
-              make_float4(acc0[db][4 * rq], acc0[db][4 * rq + 1], acc0[db][4 * rq + 2],
-                          acc0[db][4 * rq + 3]);
-          if constexpr (!DQ)
+          if constexpr (ACC0)
+            *reinterpret_cast<float4*>(po + d) =
+                make_float4(acc0[db][4 * rq], acc0[db][4 * rq + 1], acc0[db][4 * rq + 2],
+                            acc0[db][4 * rq + 3]);
+          if constexpr (ACC1)
             *reinterpret_cast<float4*>(po + D + d) =
                 make_float4(acc1[db][4 * rq], acc1[db][4 * rq + 1], acc1[db][4 * rq + 2],
                             acc1[db][4 * rq + 3]);
@@ -690,11 +709,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int d = 32 * db + 8 * rq + 4 * hh;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc0[db][4 * rq] * scale, acc0[db][4 * rq + 1] * scale);
-          w[1] = pack_bf16x2(acc0[db][4 * rq + 2] * scale, acc0[db][4 * rq + 3] * scale);
-          *reinterpret_cast<u32x2*>(g0 + d) = w;
-          if constexpr (!DQ) {
+          if constexpr (ACC0) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc0[db][4 * rq] * scale, acc0[db][4 * rq + 1] * scale);
+            w[1] = pack_bf16x2(acc0[db][4 * rq + 2] * scale, acc0[db][4 * rq + 3] * scale);
+            *reinterpret_cast<u32x2*>(g0 + d) = w;
+          }
+          if constexpr (ACC1) {
             u32x2 v;
             v[0] = pack_bf16x2(acc1[db][4 * rq], acc1[db][4 * rq + 1]);
             v[1] = pack_bf16x2(acc1[db][4 * rq + 2], acc1[db][4 * rq + 3]);
@@ -733,20 +754,37 @@ __global__ __launch_bounds__(3 * D) void bwd_global_combine_kernel(FwdArgs args,
   *dst = __builtin_bit_cast(uint16_t, (__bf16)(which == 2 ? s : s * a.scale));
 }
 
+// dK and dV as two passes (each recomputes the scores; the dK pass also dP) where the fused
+// dK/dV kind needs more registers than two waves per SIMD allow.
+template <int D>
+constexpr bool kBwdSplitDKV = BWD_SPLIT_DKV_MASK & (D / 64);
+
 template <int D, int NW, int MODE>
 hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream_t s,
                         const LaunchEvents* ev) {
-  auto timed = [&](int i, auto kernel, dim3 gr, dim3 bl, auto... xs) {
-    if (ev && (ev[i].start || ev[i].stop))
-      hipExtLaunchKernelGGL(kernel, gr, bl, 0, s, ev[i].start, ev[i].stop, 0, xs...);
+  auto launch = [&](hipEvent_t start, hipEvent_t stop, auto kernel, dim3 gr, dim3 bl,
+                    auto... xs) {
+    if (start || stop)
+      hipExtLaunchKernelGGL(kernel, gr, bl, 0, s, start, stop, 0, xs...);
     else
       hipLaunchKernelGGL(kernel, gr, bl, 0, s, xs...);
+  };
+  auto timed = [&](int i, auto kernel, dim3 gr, dim3 bl, auto... xs) {
+    launch(ev ? ev[i].start : nullptr, ev ? ev[i].stop : nullptr, kernel, gr, bl, xs...);
   };
   timed(0, attn_bwd_kernel<D, kBwdDQ, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), a, g);
   // the dK/dV partials live after the dQ partials
   FwdArgs ak = a;
   ak.part = a.part + (size_t)a.B * a.H * a.g * a.chunks * D;
-  timed(1, attn_bwd_kernel<D, kBwdDKV, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), ak, g);
+  if constexpr (kBwdSplitDKV<D>) {
+    // dK and dV in two passes (the marks of the dK/dV step bracket both)
+    launch(ev ? ev[1].start : nullptr, nullptr, attn_bwd_kernel<D, kBwdDK, NW, MODE>,
+           dim3((unsigned)grid), dim3(NW * 64), ak, g);
+    launch(nullptr, ev ? ev[1].stop : nullptr, attn_bwd_kernel<D, kBwdDV, NW, MODE>,
+           dim3((unsigned)grid), dim3(NW * 64), ak, g);
+  } else {
+    timed(1, attn_bwd_kernel<D, kBwdDKV, NW, MODE>, dim3((unsigned)grid), dim3(NW * 64), ak, g);
+  }
   const long grows = (long)a.B * a.H * a.g;
   if (grows > 0)
     timed(2, bwd_global_combine_kernel<D>, dim3((unsigned)grows), dim3(3 * D), a, g);
