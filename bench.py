@@ -262,7 +262,8 @@ def _backward_bench(args):
                        "global_combine": round(comb_ms, 5)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_bwd_kernel dK/dV kind (score, dP, dK, dV products: 8*d*E)",
+            "kernel": "attn_bwd_kernel dK/dV step (useful score, dP, dK, dV products: 8*d*E; one "
+                      "fused launch, or dK and dV passes at head dim 128)",
             "achieved": round(dkv_tf, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
