@@ -39,8 +39,8 @@ def _parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-passes", type=int, default=50,
-                    help="forward passes timed one by one after a 512 MiB write that flushes "
-                         "L2 and the MALL (0 = skip)")
+                    help="forward (or decode) calls timed one by one after a read of a 512 MiB "
+                         "buffer that flushes L2 and the MALL (0 = skip)")
     ap.add_argument("--cpu-budget-gflop", type=float, default=640.0,
                     help="fp64 work of the oracle sample: whole heads (at least one); a workload "
                          "smaller than the budget is run repeatedly")
@@ -121,6 +121,10 @@ def _decode_bench(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # cold steps: reading a 512 MiB buffer before each evicts L2 and the MALL (the step's 134 MB
+    # of window rows would otherwise stay in the 256 MB MALL between back-to-back steps)
+    cold_ms = _cold_times(step, stream, args.cold_passes) if args.cold_passes > 0 else None
+
     elem = 2 if inp.dtype == "bf16" else 4
     last = inp.positions.astype(np.int64) + inp.m - 1
     first = np.maximum(0, inp.positions.astype(np.int64) - inp.window + 1)
@@ -145,6 +149,12 @@ def _decode_bench(args):
         "config": {"workload": wl.name, "batch": inp.batch, "heads": inp.heads, "head_dim": inp.d,
                    "window": inp.window, "new_rows": inp.m, "cache_len": inp.cache_len,
                    "ring": inp.ring, "algorithmic_bytes": alg_bytes, "description": wl.note},
+        "cold_l2_mall_flushed": None if cold_ms is None else {
+            "passes": args.cold_passes, "flush_read_bytes": 512 << 20,
+            "ms_median": round(float(np.median(cold_ms)), 5),
+            "ms_p10": round(float(np.percentile(cold_ms, 10)), 5),
+            "ms_p90": round(float(np.percentile(cold_ms, 90)), 5),
+            "GB_per_s_median": round(alg_bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 1)},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_window_kernel (whole step: one launch for this shape)",
@@ -511,6 +521,27 @@ def _gates_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _cold_times(step, stream, passes):
+    """Per-call times (ms) of `passes` calls, each after a read of a 512 MiB buffer (a
+    reduction, so the caches are left holding clean lines of that buffer)."""
+    import numpy as np
+    import torch
+
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(passes)]
+    for e0, e1 in ev:
+        sink += flush.sum()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    times = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    del flush, sink
+    return times
+
+
 def _environment():
     """The GPU, its clock and the software stack the numbers were taken with."""
     import subprocess
@@ -691,23 +722,14 @@ def main():
     attn_ms, comb_ms = (float(x) for x in spans.mean(axis=0))
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # cold passes: before each, a 512 MiB write evicts the inputs from L2 and the MALL (the
-    # 256 MB last-level cache would otherwise hold a 134 MB working set); events bracket the
-    # forward alone on the launch stream
+    # cold passes: before each, reading a 512 MiB buffer evicts the inputs from L2 and the MALL
+    # (the 256 MB last-level cache would otherwise hold a 134 MB working set); a read leaves
+    # clean lines, so no write-back of the flush competes with the pass.  Events bracket the
+    # forward alone on the launch stream.
     cold = None
     if args.cold_passes > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.cold_passes)]
-        for i, (e0, e1) in enumerate(ev):
-            flush.fill_(i & 0xFF)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        cms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
-        del flush
-        cold = {"passes": args.cold_passes, "flush_bytes": 512 << 20,
+        cms = _cold_times(step, stream, args.cold_passes)
+        cold = {"passes": args.cold_passes, "flush_read_bytes": 512 << 20,
                 "ms_median": round(float(np.median(cms)), 5),
                 "ms_p10": round(float(np.percentile(cms, 10)), 5),
                 "ms_p90": round(float(np.percentile(cms, 90)), 5),
