@@ -14,6 +14,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "longattn.h")
 
 
+@pytest.fixture(scope="module", autouse=True)
+def _library_built():
+    """These tests load the library without a GPU; build it (hipcc cross-compiles for gfx950)
+    when no built copy is in the tree."""
+    if not os.path.exists(la.LIB_PATH):
+        from sparse_long_sequence_banded_amd import build
+
+        build.build()
+    yield
+
+
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
