@@ -57,19 +57,21 @@ struct Tile {
   int ks0;       // kBand window tiles: residue-subsequence index of row 0
 };
 
-// LDS stages of K tiles and of V tiles: two each (loads run one tile ahead).  At head dim 64 a
-// workgroup then needs about 36 KB of LDS, so four fit on a CU (more resident waves measured
-// faster than a third stage).
-template <int D>
-constexpr int kStages = 2;
+// LDS stages of K tiles and of V tiles: two each (loads run one tile ahead) for four-wave
+// workgroups; at head dim 64 a workgroup then needs about 36 KB of LDS, so four fit on a CU
+// (more resident waves measured faster than a third stage).  Two-wave workgroups (64-row layout
+// blocks) take one stage each and are held to 128 VGPRs: about 19 KB of LDS, so eight fit on a
+// CU, four waves per SIMD, where two stages would leave two (measured 7% faster on a 64-row
+// block layout, a few values spilled).
+constexpr int stages_of(int nw) { return nw == 2 ? 1 : 2; }
 // Key-padding bits staged in LDS per workgroup: 64-bit words covering 4096 positions.
 constexpr int kPadWords = 64;
 
 // LDS of one workgroup (either kind of work uses the same layout).
-template <int D>
+template <int D, int NS>
 struct Smem {
-  __attribute__((aligned(1024))) unsigned char stage_k[kStages<D>][kKeyTile * D * 2];
-  __attribute__((aligned(1024))) unsigned char stage_v[kStages<D>][kKeyTile * D * 2];
+  __attribute__((aligned(1024))) unsigned char stage_k[NS][kKeyTile * D * 2];
+  __attribute__((aligned(1024))) unsigned char stage_v[NS][kKeyTile * D * 2];
   int lay_list[256];                            // layout mode: valid key blocks of the row
   __attribute__((aligned(16))) int g_pos[kGlobalCap];  // global columns: positions
   unsigned long long g_valid[kGlobalCap / 64];  // global columns: usable-key bits
@@ -85,8 +87,9 @@ struct Smem {
 // first.  The work of one workgroup is a generic lambda over its kind (MODE) and its index wg
 // among that kind's workgroups; the kernel arguments stay in the kernel argument segment.
 template <int D, int NW, int QB, int MODE_MAIN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
-  __shared__ Smem<D> sm;
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 4 : 1)))
+void attn_fwd_kernel(FwdArgs args) {
+  __shared__ Smem<D, stages_of(NW)> sm;
   const FwdCore a = args;
   const int total = gridDim.x;
   const int Lid = xcd_remap(blockIdx.x, total);
@@ -135,8 +138,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     constexpr int KS = D / 16;         // MFMA k-steps over the head dim
     constexpr int DB = D / 32;         // 32-row blocks of O^T
     constexpr int MAT = kKeyTile * D * 2;
-    constexpr int NS = kStages<D>;
-    static_assert(NS == 2, "the tile schedule below uses two stages");
+    constexpr int NS = stages_of(NW);
     constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
     constexpr int LPW = NLOAD / NW;    // of which each wave issues
     constexpr int RPB = 64 / CH;       // rows per 1 KB block
@@ -317,9 +319,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     };
     const bool kwave = mat == 0;
     // Global column positions are loaded first (the staging below needs them and, with key
-    // padding, loads a pad byte at each), then the first NS-1 tiles' loads go out when they are
-    // local tiles (they need nothing from the staging), so their latency overlaps that of the Q
-    // fragments and the staging.
+    // padding, loads a pad byte at each), then tile 0's loads go out when it is a local tile (it
+    // needs nothing from the staging), so their latency overlaps that of the Q fragments and the
+    // staging.
     int gx[GREG];
     if constexpr (kHasGlobalCols) {
   #pragma unroll
@@ -328,9 +330,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
         gx[i] = (n_gtiles > 0 && c < a.g) ? gb[c] : a.n;
       }
     }
-  #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (i < n_local) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
+    if (n_local > 0) issue(kwave ? stage_k[0] : stage_v[0], tile_of(0));
 
     // Q fragments (B operands of the score MFMAs), loaded once.
     const float c2 = a.scale_log2;
@@ -429,10 +429,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
       for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[qb][s]));
     __syncthreads();
-    // gathered tiles among the first NS-1 (their rows come from the staged positions)
-  #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (i >= n_local && i < n_tiles) issue(kwave ? stage_k[i] : stage_v[i], tile_of(i));
+    // a gathered first tile (its rows come from the staged positions)
+    if (n_local == 0 && n_tiles > 0) issue(kwave ? stage_k[0] : stage_v[0], tile_of(0));
 
 
     // window mode: bits of the usable global keys among the rows of local tile t
@@ -680,19 +678,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
     };
 
     // ------------------------------------------------------------------ tile loop
-    // Two LDS stages of K tiles and two of V tiles; tile t lives in stage t % 2.  Step t: a
-    // barrier retires every read of tile t-1, whose stage then takes tile t+1's loads; each wave
-    // then waits for its own loads of tile t only (tile t+1's stay in flight: loads complete in
-    // issue order), and a second barrier makes tile t visible to every wave.  Issuing tile t+1
-    // before waiting for tile t keeps two tiles in flight whenever a load is late.  Tile 0 was
-    // issued above.
+    // Two stages: tile t lives in stage t % 2.  Step t: a barrier retires every read of tile
+    // t-1, whose stage then takes tile t+1's loads; each wave then waits for its own loads of
+    // tile t only (tile t+1's stay in flight: loads complete in issue order), and a second
+    // barrier makes tile t visible to every wave.  Issuing tile t+1 before waiting for tile t
+    // keeps two tiles in flight whenever a load is late.  One stage: the barrier that retires
+    // tile t-1 precedes tile t's loads, which are waited for at once (other workgroups on the CU
+    // cover the wait).  Tile 0 was issued above.
     if (n_tiles > 0) {
       int st = 0;  // stage of tile t
       for (int t = 0; t < n_tiles; ++t) {
-        if (t > 0) __syncthreads();  // every wave is done with tile t-1: its stage may be refilled
-        if (t + 1 < n_tiles) issue(kwave ? stage_k[st ^ 1] : stage_v[st ^ 1], tile_of(t + 1));
-        if (t + 1 < n_tiles) wait_vmcnt<LPW>();  // tile t landed; tile t+1 stays in flight
-        else wait_vmcnt<0>();
+        if constexpr (NS == 1) {
+          if (t > 0) {
+            __syncthreads();  // every wave is done with tile t-1: the stage may be refilled
+            issue(kwave ? stage_k[0] : stage_v[0], tile_of(t));
+          }
+          wait_vmcnt<0>();
+        } else {
+          if (t > 0) __syncthreads();  // every wave is done with tile t-1: its stage may be refilled
+          if (t + 1 < n_tiles) issue(kwave ? stage_k[st ^ 1] : stage_v[st ^ 1], tile_of(t + 1));
+          if (t + 1 < n_tiles) wait_vmcnt<LPW>();  // tile t landed; tile t+1 stays in flight
+          else wait_vmcnt<0>();
+        }
         __syncthreads();  // tile t visible to every wave
         const Tile T = tile_of(t);
         bool need_band = false;
@@ -705,7 +712,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs args) {
           scores(stage_k[st], sc);
           finish(sc, stage_v[st], T, vmask, need_band);
         }
-        st ^= 1;
+        if constexpr (NS == 2) st ^= 1;
       }
     }
 
