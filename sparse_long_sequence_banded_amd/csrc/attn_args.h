@@ -9,6 +9,7 @@ namespace longattn {
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
 constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
 constexpr int kGlobalChunk = 1024;    // keys per global-row partial workgroup
+constexpr int kGlobalChunkLayout = 512;  // the same in the forward pass of a block layout
 constexpr int kGlobalCap = 256;       // global tokens the bf16 kernels stage in LDS
 
 enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };
@@ -30,6 +31,7 @@ struct FwdCore {
   int band_on;
   int block, max_kb;
   int chunks;             // key chunks of the global-row partial workgroups
+  int chunk_keys;         // keys per chunk
   int grid_rows;          // global-row partial workgroups in the attention launch
   float scale;            // softmax scale (> 0)
   float scale_log2;       // scale * log2(e)

@@ -253,8 +253,8 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
         n_local = (s_hi >= s_lo) ? (s_hi - s_lo + kKeyTile) / kKeyTile : 0;
       }
     } else {
-      const int c0 = ck * kGlobalChunk;
-      const int c1 = min(a.n, c0 + kGlobalChunk);
+      const int c0 = ck * a.chunk_keys;
+      const int c1 = min(a.n, c0 + a.chunk_keys);
       n_local = (c1 > c0) ? (c1 - c0 + kKeyTile - 1) / kKeyTile : 0;
       s_lo = c0;
       s_hi = c1 - 1;

@@ -250,8 +250,8 @@ void attn_fwd_kernel(FwdArgs args) {
       __syncthreads();
       n_local = lay_cnt * tpb;
     } else {
-      const int c0 = ck * kGlobalChunk;
-      const int c1 = min(a.n, c0 + kGlobalChunk);
+      const int c0 = ck * a.chunk_keys;
+      const int c1 = min(a.n, c0 + a.chunk_keys);
       n_local = (c1 > c0) ? (c1 - c0 + kKeyTile - 1) / kKeyTile : 0;
       k_lo = c0;
       k_hi = c1 - 1;
