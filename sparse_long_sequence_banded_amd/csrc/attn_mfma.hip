@@ -523,6 +523,9 @@ void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
           for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma_32x32x16(kf, qf[qb][ks], sc[kb][qb]);
         }
+        // the first half's chain goes out whole before the second's, so its softmax can start
+        // while the matrix cores work on the second half (interleaved chains finish together)
+        if (kb == 0) __builtin_amdgcn_sched_barrier(0);
       }
     };
     // ---- masks, online softmax step and O^T += V^T P^T for one tile whose scores are in sc.
