@@ -55,6 +55,7 @@ struct Tile {
   int count;     // rows >= count do not exist (never attended; their loads return zeros or
                  // repeat a valid row)
   int ks0;       // kBand window tiles: residue-subsequence index of row 0
+  int lt;        // kBand window tiles: index of the tile within the workgroup's key range
 };
 
 // LDS stages of K tiles and of V tiles: two each (loads run one tile ahead) for four-wave
@@ -258,17 +259,33 @@ void attn_fwd_kernel(FwdArgs args) {
     }
     const int n_gtiles = (kHasGlobalCols && a.g > 0) ? (a.g + kKeyTile - 1) / kKeyTile : 0;
     const int n_tiles = n_local + n_gtiles;
+    // At head dim 64, window mode walks its key tiles in a rotated order: step t takes the tile
+    // whose index in the residue subsequence, (k_lo / 64) + lt, is congruent to t modulo
+    // n_local.  Neighbouring query tiles (whose key ranges overlap in all but two tiles) then
+    // read the same K/V tile at the same step instead of two steps apart, so the re-reads hit
+    // the XCD's L2 (about a quarter less read traffic below L2 on a 16K-token window of 256 keys
+    // each side, and about 1% faster).  The softmax does not depend on the order of the keys.
+    // The head-dim-128 kernel keeps the natural order: there the added index arithmetic alone
+    // (measured with the order unchanged, same output bits) made the 32K causal window 1.5%
+    // slower.
+    int rot = 0;
+    if constexpr (MODE == kBand && D == 64) {
+      if (n_local > 0) rot = (n_local - (k_lo / kKeyTile) % n_local) % n_local;
+    }
 
     auto tile_of = [&](int t) -> Tile {
       Tile T;
       T.ks0 = 0;
+      T.lt = 0;
       if (t >= n_local) {
         T.gathered = 1;
         T.base = (t - n_local) * kKeyTile;
         T.count = min(kKeyTile, a.g - T.base);
       } else if constexpr (MODE == kBand) {
         T.gathered = 0;
-        T.ks0 = k_lo + t * kKeyTile;
+        if constexpr (D == 64) T.lt = t + rot < n_local ? t + rot : t + rot - n_local;
+        else T.lt = t;
+        T.ks0 = k_lo + T.lt * kKeyTile;
         T.base = p + dl * T.ks0;
         T.count = min(kKeyTile, np - T.ks0);
       } else if constexpr (MODE == kLayout) {
@@ -708,7 +725,7 @@ void attn_fwd_kernel(FwdArgs args) {
         bool need_band = false;
         if (reach(T, need_band)) {
           unsigned long long vmask;
-          if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, t);
+          if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, T.lt);
           else if constexpr (kHasGlobalCols) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T);
           else vmask = local_valid(T);
           f32x16 sc[2][QB];
