@@ -168,6 +168,18 @@ def test_global_tokens_only():
     parity(inp, "globals only")
 
 
+@pytest.mark.parametrize("wl,wr", [(150, 77), (64, 64), (333, 1)])
+def test_window_tiles_in_rotated_order_with_global_keys_inside(wl, wr):
+    # head dim 64 walks each workgroup's window tiles starting at a rotated tile; many global
+    # keys fall inside the windows (their per-tile bits are indexed by the rotated tile), the
+    # per-workgroup tile count varies at the sequence ends and with the dilation, and the key
+    # range starts off the 64-key grid
+    inp = random_case(39, batch=2, heads=3, n=2000, d=64, win_left=wl, win_right=wr,
+                      dilations=[1, 2, 3], n_global=60, pad="random", pad_count=97)
+    parity(inp, f"rotated walk wl={wl} wr={wr}")
+    assert gpu_count(inp) == oracle.count_inputs(inp)
+
+
 def test_uniform_and_per_head_dilation_tables():
     for dil in (3, [1, 2, 3, 4, 5]):
         inp = random_case(37, batch=1, heads=5, n=900, d=64, win_left=17, win_right=9,
