@@ -82,6 +82,7 @@ struct STile {
   int base;
   int count;     // rows >= count do not exist
   int ks0;       // window tiles: residue-subsequence index of row 0
+  int lt;        // window tiles: index of the tile within the workgroup's streamed range
 };
 
 // Occupancy: the dQ kind is held to 168 VGPRs at d = 64 (three waves per SIMD) and 256 at
@@ -261,17 +262,28 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
     }
     const int n_gtiles = (kGathered && a.g > 0) ? (a.g + kKeyTile - 1) / kKeyTile : 0;
     const int n_tiles = n_local + n_gtiles;
+    // At head dim 64 the window tiles are streamed in a rotated order: step t takes the tile
+    // whose residue-subsequence index, (s_lo / 64) + lt, is congruent to t modulo n_local, so
+    // neighbouring owner tiles read the same streamed tile at the same step and the re-reads hit
+    // the XCD's L2 (the same walk as the forward pass; the sums do not depend on the order).
+    int rot = 0;
+    if constexpr (MODE == kBand && D == 64) {
+      if (n_local > 0) rot = (n_local - (s_lo / kKeyTile) % n_local) % n_local;
+    }
 
     auto tile_of = [&](int t) -> STile {
       STile T;
       T.ks0 = 0;
+      T.lt = 0;
       if (t >= n_local) {
         T.gathered = 1;
         T.base = (t - n_local) * kKeyTile;
         T.count = min(kKeyTile, a.g - T.base);
       } else if constexpr (MODE == kBand) {
         T.gathered = 0;
-        T.ks0 = s_lo + t * kKeyTile;
+        if constexpr (D == 64) T.lt = t + rot < n_local ? t + rot : t + rot - n_local;
+        else T.lt = t;
+        T.ks0 = s_lo + T.lt * kKeyTile;
         T.base = p + dl * T.ks0;
         T.count = min(kKeyTile, np - T.ks0);
       } else if constexpr (MODE == kLayout) {
@@ -667,10 +679,10 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
           // rows (dK/dV: those rows are streamed from the global list)
           unsigned long long vmask;
           if constexpr (MODE == kBand)
-            vmask = T.gathered ? sm.g_valid[T.base >> 6] : local_valid(T) & ~global_rows(T, t);
+            vmask = T.gathered ? sm.g_valid[T.base >> 6] : local_valid(T) & ~global_rows(T, T.lt);
           else if constexpr (MODE == kLayout)
             vmask = T.gathered ? sm.g_valid[T.base >> 6]
-                               : (DQ ? local_valid(T) : local_valid(T) & ~global_rows(T, t));
+                               : (DQ ? local_valid(T) : local_valid(T) & ~global_rows(T, T.lt));
           else
             vmask = local_valid(T);
           compute(st, T, vmask, need_band);
