@@ -276,6 +276,31 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
+def _launch_on(stream):
+    """Handle of the stream a helper launches on.  A stream other than the current one first
+    waits for the current one, which holds the helper's own preparation (zeroed counters,
+    contiguous copies of index tensors) and the caller's preceding work."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    if stream is not None and stream != cur:
+        stream.wait_stream(cur)
+    return _stream_handle(stream)
+
+
+def _used_on(stream, *tensors):
+    """Tensors allocated on the current stream and used by a launch on another ``stream``: tell
+    the caching allocator, so that their memory is not handed out again before that stream has
+    finished with it."""
+    import torch
+
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(stream)
+
+
 def make_desc(q, *, scale: Optional[float] = None, win_left: int = -1, win_right: int = -1,
               dilation=None, global_idx=None, key_pad=None, block_layout=None, block: int = 0):
     """Build the descriptor for q of shape [B, H, n, d].  Returns (desc, keepalive)."""
@@ -358,7 +383,7 @@ def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    sh = _stream_handle(stream)
+    sh = _launch_on(stream)
     if gate is not None:
         if gate.shape != q.shape or gate.dtype != q.dtype or not gate.is_contiguous():
             raise ValueError("gate must be a contiguous tensor of q's shape and dtype")
@@ -374,6 +399,7 @@ def forward(q, k, v, *, scale: Optional[float] = None, win_left: int = -1,
         st = longattn_forward_marked(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      out.data_ptr(), _ptr(lse),
                                      _ptr(workspace) if ws_bytes else None, ws_bytes, sh, marks)
+    _used_on(stream, out, lse, workspace, gate, *keep)
     del keep
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_forward")
@@ -410,7 +436,8 @@ def backward(q, k, v, out, lse, dout, *, scale: Optional[float] = None, win_left
     st = longattn_backward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                            dv.data_ptr(), _ptr(workspace) if ws_bytes else None, ws_bytes,
-                           _stream_handle(stream))
+                           _launch_on(stream))
+    _used_on(stream, dq, dk, dv, workspace, *keep)
     del keep
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_backward")
@@ -427,10 +454,13 @@ def count_entries(q, *, win_left: int = -1, win_right: int = -1, dilation=None,
                            global_idx=global_idx, key_pad=key_pad, block_layout=block_layout,
                            block=block)
     e = torch.zeros(2, dtype=torch.int64, device=q.device)
-    st = longattn_count_entries(desc, e.data_ptr(), _stream_handle(stream))
+    st = longattn_count_entries(desc, e.data_ptr(), _launch_on(stream))
+    _used_on(stream, e, *keep)
     del keep
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_count_entries")
+    if stream is not None:
+        stream.synchronize()  # the counts were written on that stream
     vals = e.cpu().tolist()
     return int(vals[0]), int(vals[1])
 
@@ -505,7 +535,8 @@ def decode(q, k_cache, v_cache, positions, *, window: int, scale: Optional[float
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = longattn_decode(desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                          out.data_ptr(), _ptr(lse), _ptr(workspace) if ws_bytes else None,
-                         ws_bytes, _stream_handle(stream))
+                         ws_bytes, _launch_on(stream))
+    _used_on(stream, out, lse, workspace, positions)
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_decode")
     return out, lse
@@ -569,7 +600,7 @@ def tglobal(x, gamma, wk, wv, q, k, v, bias_local, bias_side, *, radius: int = 1
     side_v = torch.empty_like(side_k)
     side_valid = torch.empty((B, G), dtype=torch.uint8, device=q.device)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    sh = _stream_handle(stream)
+    sh = _launch_on(stream)
     st = longattn_tglobal_side(desc, x.data_ptr(), gamma.data_ptr(), wk.data_ptr(),
                                wv.data_ptr(), side_k.data_ptr(), side_v.data_ptr(),
                                side_valid.data_ptr(), ws.data_ptr(), ws_bytes, sh)
@@ -581,6 +612,7 @@ def tglobal(x, gamma, wk, wv, q, k, v, bias_local, bias_side, *, radius: int = 1
                                   side_k.data_ptr(), side_v.data_ptr(), side_valid.data_ptr(),
                                   bias_local.data_ptr(), bias_side.data_ptr(), out.data_ptr(),
                                   _ptr(lse), ws.data_ptr(), ws_bytes, sh)
+    _used_on(stream, out, lse, ws, side_k, side_v, side_valid)
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_tglobal_forward")
     return out, lse, side_k, side_v, side_valid
@@ -602,7 +634,7 @@ def gate_lowrank(out, w_down, w_up, stream=None):
         raise ValueError("w_down must be [r, H*d] and w_up [H*d, r]")
     desc = longattn_gate_desc(batch=B, heads=H, n=n, d=d, rank=r)
     st = longattn_gate_lowrank(desc, out.data_ptr(), w_down.data_ptr(), w_up.data_ptr(),
-                               _stream_handle(stream))
+                               _launch_on(stream))
     if st != LONGATTN_OK:
         raise LongAttnError(st, "longattn_gate_lowrank")
     return out

@@ -24,7 +24,7 @@ struct FwdCore {
   const int32_t* gidx;    // [B][g] or null
   const uint8_t* kpad;    // [B][n] or null
   const int32_t* layout;  // [H][n/block][max_kb] or null
-  float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
+  float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][3] (m, l, e)
   const uint16_t* gate;   // elementwise output-gate logits [B][H][n][d] (out *= sigmoid), or null
   int B, H, n, g;
   int wl, wr;             // window extents clamped to n; band_on == 0 means no window

@@ -499,8 +499,11 @@ void attn_fwd_kernel(FwdArgs args) {
 
     // ------------------------------------------------------------------ running state
     // Per row: ref = the exponent offset all weights of the row are taken against (log2 units),
-    // has = some allowed key has been seen, l = sum of the weights 2^(c2 s - ref), o = the weighted
-    // sum of value rows (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4).
+    // has = some allowed key has been seen, o = the sum of value rows weighted by the bf16-rounded
+    // weights 2^(c2 s - ref) (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4),
+    // l = the sum of those rounded weights (o / l is the output: the weights that multiply the
+    // value rows add up to one, so a row dominated by a few keys carries no rounding bias),
+    // e = the sum of the weights before rounding (for lse).
     f32x16 o[QB][DB];
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -508,12 +511,13 @@ void attn_fwd_kernel(FwdArgs args) {
       for (int db = 0; db < DB; ++db)
   #pragma unroll
         for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-    float ref[QB], l_run[QB];
+    float ref[QB], l_run[QB], e_run[QB];
     bool has[QB];
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       ref[qb] = 0.f;
       l_run[qb] = 0.f;
+      e_run[qb] = 0.f;
       has[qb] = false;
     }
 
@@ -590,12 +594,12 @@ void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t pk[QB][8];
-        float part[QB];
+        float part[QB], epart[QB];
         auto exponentiate = [&]() {
   #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const float nr = -ref[qb];
-            float la = 0.f, lb = 0.f;
+            float la = 0.f, lb = 0.f, ea = 0.f, eb = 0.f;
   #pragma unroll
             for (int r = 0; r < 16; r += 4) {
               const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
@@ -604,10 +608,13 @@ void attn_fwd_kernel(FwdArgs args) {
               const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
               pk[qb][r >> 1] = pack_bf16x2(p0, p1);
               pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
-              la += p0 + p1;
-              lb += p2 + p3;
+              la = add_bf16x2(pk[qb][r >> 1], la);  // rounded weights, as the PV products use
+              lb = add_bf16x2(pk[qb][(r >> 1) + 1], lb);
+              ea += p0 + p1;  // weights before rounding
+              eb += p2 + p3;
             }
             part[qb] = la + lb;
+            epart[qb] = ea + eb;
           }
         };
         bool no_ref = false;
@@ -651,6 +658,7 @@ void attn_fwd_kernel(FwdArgs args) {
               ref[qb] = nref;
               has[qb] = has[qb] || need[qb];
               l_run[qb] *= alpha;
+              e_run[qb] *= alpha;
   #pragma unroll
               for (int db = 0; db < DB; ++db)
   #pragma unroll
@@ -660,7 +668,10 @@ void attn_fwd_kernel(FwdArgs args) {
           exponentiate();
         }
   #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
+        for (int qb = 0; qb < QB; ++qb) {
+          l_run[qb] += part[qb];
+          e_run[qb] += epart[qb];
+        }
         // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
   #pragma unroll
         for (int gh = 0; gh < 2; ++gh) {
@@ -740,6 +751,7 @@ void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = l_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(l_run[qb]), 32));
+      const float e_tot = e_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(e_run[qb]), 32));
       if (qpos[qb] < 0) continue;
       if constexpr (MODE == kGlobalRows) {
         const int c = rg * QT + wave * RW + 32 * qb + qj;
@@ -755,9 +767,10 @@ void attn_fwd_kernel(FwdArgs args) {
                             o[qb][db][4 * rq + 3]);
           }
         if (hh == 0) {
-          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
+          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 3;
           pml[0] = has[qb] ? ref[qb] : neg_inf();
           pml[1] = l_tot;
+          pml[2] = e_tot;
         }
       } else {
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
@@ -785,7 +798,7 @@ void attn_fwd_kernel(FwdArgs args) {
           }
         if (a.lse && hh == 0)
           a.lse[bh * a.n + qpos[qb]] =
-              (l_tot > 0.f) ? (ref[qb] + __log2f(l_tot)) * kLn2 : neg_inf();
+              (e_tot > 0.f) ? (ref[qb] + __log2f(e_tot)) * kLn2 : neg_inf();
       }
     }
   };
@@ -806,7 +819,7 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   constexpr int CG = kCombineThreads / QPR;     // chunk groups
   constexpr float kNegInf = -__builtin_inff();
   __shared__ float4 part[CG][QPR];
-  __shared__ float gmax[CG], gsum[CG];
+  __shared__ float gmax[CG], gsum[CG], gexact[CG];
   const FwdCore a = args;
   const int t = threadIdx.x;
   const long rows = (long)a.B * a.H * a.g;
@@ -818,14 +831,16 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   if (pos < 0 || pos >= a.n) return;  // out-of-range global index: nothing to write (uniform)
   const int K = a.chunks;
   const float* po = a.part + row * K * D;
-  const float* pml = a.part + rows * K * D + row * K * 2;
+  const float* pml = a.part + rows * K * D + row * K * 3;
   const int cg = t / QPR, cq = t % QPR;
-  float m = kNegInf, l = 0.f;                 // running max and normaliser of this thread
+  // running max, normaliser (rounded weights) and exact weight sum of this thread
+  float m = kNegInf, l = 0.f, e = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int k = cg; k < K; k += CG) {
-    const float mk = pml[2 * k];
-    const float lk = pml[2 * k + 1];
+    const float mk = pml[3 * k];
+    const float lk = pml[3 * k + 1];
+    const float ek = pml[3 * k + 2];
     const float4 v = *reinterpret_cast<const float4*>(po + (long)k * D + 4 * cq);
     if (mk == kNegInf) continue;  // chunk with no key: o = 0, l = 0
     const float mn = fmaxf(m, mk);
@@ -835,19 +850,21 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
     acc.z = acc.z * s_old + v.z * s_new;
     acc.w = acc.w * s_old + v.w * s_new;
     l = l * s_old + lk * s_new;
+    e = e * s_old + ek * s_new;
     m = mn;
   }
   part[cg][cq] = acc;
   if (cq == 0) {
     gmax[cg] = m;
     gsum[cg] = l;
+    gexact[cg] = e;
   }
   __syncthreads();
   if (t < QPR) {
     float M = kNegInf;
     for (int gi = 0; gi < CG; ++gi) M = fmaxf(M, gmax[gi]);
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
+    float L = 0.f, Le = 0.f;
     if (M != kNegInf) {
       for (int gi = 0; gi < CG; ++gi) {
         if (gmax[gi] == kNegInf) continue;
@@ -858,6 +875,7 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
         o.z += w * v.z;
         o.w += w * v.w;
         L += w * gsum[gi];
+        Le += w * gexact[gi];
       }
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -872,7 +890,7 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) orow[e] = __builtin_bit_cast(uint16_t, (__bf16)y[e]);
-    if (a.lse && t == 0) a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+    if (a.lse && t == 0) a.lse[bh * a.n + pos] = (Le > 0.f) ? (M + __log2f(Le)) * kLn2 : kNegInf;
   }
 }
 

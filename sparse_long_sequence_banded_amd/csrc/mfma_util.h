@@ -33,6 +33,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (one dot product with (1, 1)).  Softmax rows sum
+// the weights after their rounding to bf16, the values the matrix cores multiply with the value
+// rows, so that the normalised weights of a row add up to one.
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  constexpr uint32_t kOnes = 0x3f803f80u;  // (1.0, 1.0) in bf16
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, kOnes), acc, false);
+}
+
 // sigmoid(x) = 1 / (1 + e^-x), from the hardware exp2 and reciprocal (saturates to 0 and 1).
 __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.f + exp2_fast(-1.44269504088896340736f * x));

@@ -100,15 +100,26 @@ def test_workload_backward_parity(name):
     check(make_inputs(workload(name)), 70, name)
 
 
-@pytest.mark.parametrize("name,heads", [("dilated_16k", [0, 5])])
-def test_workload_backward_sampled_heads(name, heads):
-    _note(f"[backward] {name} full launch, oracle on heads {heads}")
-    check(make_inputs(workload(name)), 71, name, heads)
+@pytest.mark.parametrize("name", ["dilated_16k", "swa512_causal_32k"])
+def test_workload_backward_full_size_every_head(name):
+    """Full-size launch; dQ, dK and dV of every head compared with the oracle element by element
+    (the 32K causal window at head dim 128 is the long-context fine-tuning shape)."""
+    _note(f"[backward] {name} full launch, oracle on every head")
+    check(make_inputs(workload(name)), 71, name)
+
+
+@pytest.mark.parametrize("wl,wr", [(150, 77), (333, 1)])
+def test_backward_rotated_window_walk_with_global_keys_inside(wl, wr):
+    """Head dim 64 walks each workgroup's window tiles from a rotated start; the per-tile bits of
+    the global keys inside the windows are indexed by the rotated tile, the tile count varies at
+    the sequence ends and with the dilation, and the key ranges start off the 64-key grid."""
+    inp = random_case(79, batch=2, heads=3, n=2000, d=64, win_left=wl, win_right=wr,
+                      dilations=[1, 2, 3], n_global=60, pad="random", pad_count=97)
+    check(inp, 79, f"rotated walk wl={wl} wr={wr}")
 
 
 def test_causal_512_window_backward():
-    """The causal 512-key window at head dim 128 (the SWA decoder layers' shape) on 4096
-    positions; the oracle runs one thread per head, so the 32K workload is not checked whole."""
+    """The causal 512-key window at head dim 128 on 4096 positions with two heads."""
     inp = random_case(72, batch=1, heads=2, n=4096, d=128, win_left=511, win_right=0)
     check(inp, 72, "causal 512, d128")
 

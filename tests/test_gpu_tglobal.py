@@ -168,3 +168,60 @@ def test_tglobal_full_size_sampled_heads():
     e = _close(out[:, heads], ref_out, "out")
     _lse_close(lse[:, heads], ref_lse, "lse", LSE_ATOL_PIPELINE)
     _note(f"[tglobal] {wl.name}: max-abs {e:.3e}")
+
+
+@pytest.mark.parametrize("variant", ["late_side_key", "scaled"])
+def test_tglobal_attention_with_wide_score_ranges(variant):
+    """Rows whose scores force the attention kernel's online softmax to move its reference.
+
+    The kernel walks a row's local window tiles before its global-token tiles and keeps the
+    weights of a tile against the row's reference while a lane's 16 weights of a half sum to at
+    most 2^16.  "late_side_key": every query gains 8 e0 and global token 0 of each (b, h) has key
+    60 e0, so it scores about 60 natural units while the local keys stay within a few units; the
+    host check on fp64 scores shows a margin of at least 20 natural units beyond both bias tables'
+    reach, so the reference must move on the first global-token tile.  "scaled": Q and K drawn
+    at 3x (score std about 9 natural units), so rows span far more than 16 log2 units."""
+    kw = dict(batch=2, heads=2, n=1000, d=64, d_model=64, radius=127, block=16,
+              pad_tail=(0, 77))
+    inp = make_tglobal_inputs(97, **kw)
+    G = max(1, inp.n // inp.block)
+    rng = np.random.default_rng(98)
+    sk = rng.standard_normal((inp.batch, inp.heads, G, inp.d), dtype=np.float32)
+    sv = rng.standard_normal((inp.batch, inp.heads, G, inp.d), dtype=np.float32)
+    q = bf16_bits_to_f32(inp.q).copy()
+    k = bf16_bits_to_f32(inp.k).copy()
+    if variant == "late_side_key":
+        q[..., 0] += 8.0
+        sk[:, :, 0, :] = 0.0
+        sk[:, :, 0, 0] = 60.0
+    else:
+        q *= 3.0
+        k *= 3.0
+    inp.q, inp.k = round_to_bf16_bits(q), round_to_bf16_bits(k)
+    sk_b, sv_b = round_to_bf16_bits(sk), round_to_bf16_bits(sv)
+    valid = np.ones((inp.batch, G), np.uint8)
+    valid[:, 1::3] = 0
+    # host check on fp64 scores (natural units; each bias table adds at most bmax)
+    qf, kf = inp.f64("q"), inp.f64("k")
+    skf = bf16_bits_to_f32(sk_b).astype(np.float64)
+    bmax = float(max(np.abs(inp.bias_local).max(), np.abs(inp.bias_side).max()))
+    rows = np.random.default_rng(99).integers(0, inp.n, size=60)
+    spans = []
+    for i in rows:
+        lo, hi = max(0, i - inp.radius), min(inp.n - 1, i + inp.radius)
+        for b in range(inp.batch):
+            for h in range(inp.heads):
+                loc = inp.scale * (kf[b, h, lo:hi + 1] @ qf[b, h, i])
+                if variant == "late_side_key":
+                    big = inp.scale * float(skf[b, h, 0] @ qf[b, h, i])
+                    assert big - loc.max() - 2 * bmax >= 20.0, (b, h, i)
+                else:
+                    spans.append(float(loc.max() - loc.min()) * 1.4426950408889634)
+    if spans:
+        assert np.median(spans) > 32.0, np.median(spans)
+    out, lse, *_ = run_gpu(inp, side=(sk_b, sv_b, valid))
+    ref_out, ref_lse, _ = oracle_attention(inp, skf, bf16_bits_to_f32(sv_b).astype(np.float64),
+                                           valid)
+    e = _close(out, ref_out, "out")
+    _lse_close(lse, ref_lse, "lse")
+    _note(f"[tglobal attention] {variant}: max-abs {e:.3e}")
