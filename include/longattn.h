@@ -129,6 +129,22 @@ typedef struct {
 longattn_status longattn_gate_lowrank(const longattn_gate_desc* desc, void* out,
                                       const void* w_down, const void* w_up, void* stream);
 
+/* The forward pass without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments and result as longattn_forward without the workspace; allocates nothing.  The
+ * scratch it needs (the global rows' partial results) lives in a device array of the library's
+ * own, LONGATTN_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the process ends.  A
+ * descriptor whose longattn_workspace_size exceeds that returns LONGATTN_ERR_WORKSPACE and
+ * launches nothing.  Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads) race and must be serialised by the caller; calls in
+ * order on one stream are safe (each pass writes every partial it reads).  The first call on
+ * each GPU resolves the array's device address (a runtime query, no allocation); make it before
+ * capturing a graph.  LONGATTN_DEBUG checks are not run by this entry point. */
+#define LONGATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+longattn_status longattn_forward_noalloc(const longattn_desc* desc, const void* q,
+                                         const void* k, const void* v, void* out, float* lse,
+                                         void* stream);
+
 /* Useful score entries, counted on the GPU: entries_out is a DEVICE int64[2] that receives
  * [0] E = sum over all (b, h, i) of |S(b, h, i)| and [1] the part of E in global-token rows
  * (asynchronous on `stream`).  4 * d * E is the useful floating-point work of one forward pass

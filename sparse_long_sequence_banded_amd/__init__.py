@@ -35,6 +35,7 @@ EXPORTED = (
     "longattn_workspace_size",
     "longattn_forward",
     "longattn_forward_marked",
+    "longattn_forward_noalloc",
     "longattn_count_entries",
     "longattn_forward_gated",
     "longattn_backward_workspace_size",
@@ -153,6 +154,8 @@ def load():
             lib.longattn_forward_marked.argtypes = [D, P, P, P, P, P, P, ctypes.c_size_t, P,
                                                     ctypes.POINTER(P), ctypes.c_int32]
             lib.longattn_forward_marked.restype = ctypes.c_int
+            lib.longattn_forward_noalloc.argtypes = [D, P, P, P, P, P, P]
+            lib.longattn_forward_noalloc.restype = ctypes.c_int
             lib.longattn_count_entries.argtypes = [D, P, P]
             lib.longattn_count_entries.restype = ctypes.c_int
             lib.longattn_forward_gated.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -214,6 +217,15 @@ def longattn_forward_marked(desc, q, k, v, out, lse, workspace, workspace_bytes,
         arr = (ctypes.c_void_p * n)(*marks)
     return load().longattn_forward_marked(ctypes.byref(desc), q, k, v, out, lse, workspace,
                                           int(workspace_bytes), stream, arr, n)
+
+
+def longattn_forward_noalloc(desc, q, k, v, out, lse, stream) -> int:
+    """Raw call of the allocation-free forward pass (scratch in the library's own device array
+    of LONGATTN_NOALLOC_SCRATCH_BYTES per GPU; calls that overlap on one GPU race)."""
+    return load().longattn_forward_noalloc(ctypes.byref(desc), q, k, v, out, lse, stream)
+
+
+LONGATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def longattn_count_entries(desc, entries_out, stream) -> int:

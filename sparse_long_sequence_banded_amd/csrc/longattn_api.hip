@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "attn_args.h"
@@ -380,7 +381,7 @@ namespace {
 longattn_status forward_impl(const longattn_desc* desc, const void* q, const void* k,
                              const void* v, const void* gate, void* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* marks, int32_t n_marks) {
+                             void* const* marks, int32_t n_marks, bool debug_allowed = true) {
   if (n_marks != 0 && n_marks != LONGATTN_N_MARKS) return LONGATTN_ERR_INVALID_ARG;
   if (n_marks && !marks) return LONGATTN_ERR_INVALID_ARG;
   Plan p;
@@ -401,7 +402,7 @@ longattn_status forward_impl(const longattn_desc* desc, const void* q, const voi
     return LONGATTN_ERR_ALIGNMENT;
   if (gate && !aligned16(gate)) return LONGATTN_ERR_ALIGNMENT;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return LONGATTN_ERR_WORKSPACE;
-  if (debug_enabled()) {
+  if (debug_allowed && debug_enabled()) {
     st = debug_check(desc, s);
     if (st != LONGATTN_OK) return st;
   }
@@ -465,6 +466,63 @@ longattn_status longattn_forward_gated(const longattn_desc* desc, const void* q,
   if (!gate) return LONGATTN_ERR_INVALID_ARG;
   return forward_impl(desc, q, k, v, gate, out, lse, workspace, workspace_bytes, stream,
                       nullptr, 0);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------ no allocation
+// Scratch of longattn_forward_noalloc: the global-row partials of a forward pass, in a device
+// array of the library's own.  Each GPU the library runs on holds one copy of it until the
+// process ends.  Host code must not take the array's address directly (on the host, its name
+// stands for a host-side shadow): each device's address comes from hipGetSymbolAddress, resolved
+// once per device with that device current and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[LONGATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream` (the current device for the
+// null stream).
+longattn_status scratch_for(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LONGATTN_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return LONGATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return LONGATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return LONGATTN_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return LONGATTN_ERR_HIP;
+    if (e != hipSuccess || !ptr) return LONGATTN_ERR_HIP;
+    scratch_addr[dev] = ptr;
+  }
+  *out = scratch_addr[dev];
+  return LONGATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+longattn_status longattn_forward_noalloc(const longattn_desc* desc, const void* q, const void* k,
+                                         const void* v, void* out, float* lse, void* stream) {
+  Plan p;
+  longattn_status st = plan_call(desc, true, &p, forward_chunk_keys(desc));
+  if (st != LONGATTN_OK) return st;
+  if (p.ws_bytes > (size_t)LONGATTN_NOALLOC_SCRATCH_BYTES) return LONGATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0 && !p.empty) {
+    st = scratch_for(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (st != LONGATTN_OK) return st;
+  }
+  // every partial the combine reads is written by the same pass first: nothing to clear
+  return forward_impl(desc, q, k, v, nullptr, out, lse, ws, p.ws_bytes, stream, nullptr, 0,
+                      /*debug_allowed=*/false);
 }
 
 longattn_status longattn_count_entries(const longattn_desc* desc, int64_t* entries_out,
