@@ -24,7 +24,7 @@ struct FwdCore {
   const int32_t* gidx;    // [B][g] or null
   const uint8_t* kpad;    // [B][n] or null
   const int32_t* layout;  // [H][n/block][max_kb] or null
-  float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][3] (m, l, e)
+  float* part;            // global-row partials: [B*H][g][chunks][D] o, then [..][2] (m, l)
   const uint16_t* gate;   // elementwise output-gate logits [B][H][n][d] (out *= sigmoid), or null
   int B, H, n, g;
   int wl, wr;             // window extents clamped to n; band_on == 0 means no window
@@ -130,6 +130,7 @@ struct LaunchEvents {
 hipError_t launch_attention(const FwdArgs& a, int d, int mode, long grid, hipStream_t s,
                             const LaunchEvents& ev);
 hipError_t launch_global_combine(const FwdArgs& a, int d, hipStream_t s, const LaunchEvents& ev);
+
 hipError_t launch_rowwise_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_count_entries(const FwdArgs& a, int64_t* out, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t s);

@@ -78,6 +78,7 @@ struct Smem {
   unsigned long long g_valid[kGlobalCap / 64];  // global columns: usable-key bits
   unsigned long long g_bits[kPadWords];         // window mode: global keys among window keys
   unsigned long long pad_bits[kPadWords];       // key padding of the reachable positions
+  unsigned long long tmask[kPadWords];          // allowed-key bits of each local tile
   int lay_cnt;
 };
 
@@ -290,10 +291,12 @@ void attn_fwd_kernel(FwdArgs args) {
         T.count = min(kKeyTile, np - T.ks0);
       } else if constexpr (MODE == kLayout) {
         T.gathered = 0;
+        T.lt = t;
         T.base = lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
         T.count = kKeyTile;
       } else {
         T.gathered = 0;
+        T.lt = t;
         T.base = k_lo + t * kKeyTile;
         T.count = min(kKeyTile, k_hi + 1 - T.base);
       }
@@ -477,6 +480,20 @@ void attn_fwd_kernel(FwdArgs args) {
       }
       return __ballot(ok);
     };
+    // The allowed-key bits of every local tile (existing, not padded, and in window mode not a
+    // global key), computed once per workgroup (tile lt by wave lt % NW) when they fit; the first
+    // tile barrier of the loop publishes them.
+    const bool tmask_staged = n_local <= kPadWords;
+    if (tmask_staged) {
+      for (int t = wave; t < n_local; t += NW) {
+        int lt = t;
+        if constexpr (MODE == kBand && D == 64) lt = t + rot < n_local ? t + rot : t + rot - n_local;
+        const Tile T = tile_of(t);
+        unsigned long long m = local_valid(T);
+        if constexpr (MODE == kBand) m &= ~global_keys(T, lt);
+        if (lane == 0) sm.tmask[lt] = m;
+      }
+    }
 
     // ------------------------------------------------------------------ per-lane LDS read offsets
     // K operand of S^T for key block kb, k-step ks: row 32kb + qj, logical chunk 2ks + hh.
@@ -501,9 +518,8 @@ void attn_fwd_kernel(FwdArgs args) {
     // Per row: ref = the exponent offset all weights of the row are taken against (log2 units),
     // has = some allowed key has been seen, o = the sum of value rows weighted by the bf16-rounded
     // weights 2^(c2 s - ref) (transposed: o[qb][db][r] is column 32db + 8(r/4) + 4hh + r%4),
-    // l = the sum of those rounded weights (o / l is the output: the weights that multiply the
-    // value rows add up to one, so a row dominated by a few keys carries no rounding bias),
-    // e = the sum of the weights before rounding (for lse).
+    // l = the sum of those rounded weights: o / l is the output, so the weights that multiply the
+    // value rows add up to one and a row dominated by a few keys carries no rounding bias.
     f32x16 o[QB][DB];
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -511,13 +527,12 @@ void attn_fwd_kernel(FwdArgs args) {
       for (int db = 0; db < DB; ++db)
   #pragma unroll
         for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-    float ref[QB], l_run[QB], e_run[QB];
+    float ref[QB], l_run[QB];
     bool has[QB];
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       ref[qb] = 0.f;
       l_run[qb] = 0.f;
-      e_run[qb] = 0.f;
       has[qb] = false;
     }
 
@@ -594,12 +609,12 @@ void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t pk[QB][8];
-        float part[QB], epart[QB];
+        float part[QB];
         auto exponentiate = [&]() {
   #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const float nr = -ref[qb];
-            float la = 0.f, lb = 0.f, ea = 0.f, eb = 0.f;
+            float la = 0.f, lb = 0.f;
   #pragma unroll
             for (int r = 0; r < 16; r += 4) {
               const float p0 = exp2_fast(__builtin_fmaf(sc[kb][qb][r], c2, nr));
@@ -608,13 +623,10 @@ void attn_fwd_kernel(FwdArgs args) {
               const float p3 = exp2_fast(__builtin_fmaf(sc[kb][qb][r + 3], c2, nr));
               pk[qb][r >> 1] = pack_bf16x2(p0, p1);
               pk[qb][(r >> 1) + 1] = pack_bf16x2(p2, p3);
-              la = add_bf16x2(pk[qb][r >> 1], la);  // rounded weights, as the PV products use
+              la = add_bf16x2(pk[qb][r >> 1], la);  // the rounded weights the PV products use
               lb = add_bf16x2(pk[qb][(r >> 1) + 1], lb);
-              ea += p0 + p1;  // weights before rounding
-              eb += p2 + p3;
             }
             part[qb] = la + lb;
-            epart[qb] = ea + eb;
           }
         };
         bool no_ref = false;
@@ -658,7 +670,6 @@ void attn_fwd_kernel(FwdArgs args) {
               ref[qb] = nref;
               has[qb] = has[qb] || need[qb];
               l_run[qb] *= alpha;
-              e_run[qb] *= alpha;
   #pragma unroll
               for (int db = 0; db < DB; ++db)
   #pragma unroll
@@ -668,10 +679,7 @@ void attn_fwd_kernel(FwdArgs args) {
           exponentiate();
         }
   #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          l_run[qb] += part[qb];
-          e_run[qb] += epart[qb];
-        }
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
         // ---- O^T += V^T P^T for the 16-key groups 2kb, 2kb+1
   #pragma unroll
         for (int gh = 0; gh < 2; ++gh) {
@@ -736,8 +744,9 @@ void attn_fwd_kernel(FwdArgs args) {
         bool need_band = false;
         if (reach(T, need_band)) {
           unsigned long long vmask;
-          if constexpr (MODE == kBand) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T) & ~global_keys(T, T.lt);
-          else if constexpr (kHasGlobalCols) vmask = T.gathered ? g_valid[T.base >> 6] : local_valid(T);
+          if (T.gathered) vmask = g_valid[T.base >> 6];
+          else if (tmask_staged) vmask = sm.tmask[T.lt];
+          else if constexpr (MODE == kBand) vmask = local_valid(T) & ~global_keys(T, T.lt);
           else vmask = local_valid(T);
           f32x16 sc[2][QB];
           scores(stage_k[st], sc);
@@ -751,7 +760,6 @@ void attn_fwd_kernel(FwdArgs args) {
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = l_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(l_run[qb]), 32));
-      const float e_tot = e_run[qb] + __uint_as_float(__shfl_xor(__float_as_uint(e_run[qb]), 32));
       if (qpos[qb] < 0) continue;
       if constexpr (MODE == kGlobalRows) {
         const int c = rg * QT + wave * RW + 32 * qb + qj;
@@ -767,10 +775,9 @@ void attn_fwd_kernel(FwdArgs args) {
                             o[qb][db][4 * rq + 3]);
           }
         if (hh == 0) {
-          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 3;
+          float* pml = a.part + (long)a.B * a.H * a.g * a.chunks * D + slot * 2;
           pml[0] = has[qb] ? ref[qb] : neg_inf();
           pml[1] = l_tot;
-          pml[2] = e_tot;
         }
       } else {
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
@@ -798,7 +805,7 @@ void attn_fwd_kernel(FwdArgs args) {
           }
         if (a.lse && hh == 0)
           a.lse[bh * a.n + qpos[qb]] =
-              (e_tot > 0.f) ? (ref[qb] + __log2f(e_tot)) * kLn2 : neg_inf();
+              (l_tot > 0.f) ? (ref[qb] + __log2f(l_tot)) * kLn2 : neg_inf();
       }
     }
   };
@@ -819,7 +826,7 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   constexpr int CG = kCombineThreads / QPR;     // chunk groups
   constexpr float kNegInf = -__builtin_inff();
   __shared__ float4 part[CG][QPR];
-  __shared__ float gmax[CG], gsum[CG], gexact[CG];
+  __shared__ float gmax[CG], gsum[CG];
   const FwdCore a = args;
   const int t = threadIdx.x;
   const long rows = (long)a.B * a.H * a.g;
@@ -831,16 +838,14 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   if (pos < 0 || pos >= a.n) return;  // out-of-range global index: nothing to write (uniform)
   const int K = a.chunks;
   const float* po = a.part + row * K * D;
-  const float* pml = a.part + rows * K * D + row * K * 3;
+  const float* pml = a.part + rows * K * D + row * K * 2;
   const int cg = t / QPR, cq = t % QPR;
-  // running max, normaliser (rounded weights) and exact weight sum of this thread
-  float m = kNegInf, l = 0.f, e = 0.f;
+  float m = kNegInf, l = 0.f;                 // running max and normaliser of this thread
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int k = cg; k < K; k += CG) {
-    const float mk = pml[3 * k];
-    const float lk = pml[3 * k + 1];
-    const float ek = pml[3 * k + 2];
+    const float mk = pml[2 * k];
+    const float lk = pml[2 * k + 1];
     const float4 v = *reinterpret_cast<const float4*>(po + (long)k * D + 4 * cq);
     if (mk == kNegInf) continue;  // chunk with no key: o = 0, l = 0
     const float mn = fmaxf(m, mk);
@@ -850,21 +855,19 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
     acc.z = acc.z * s_old + v.z * s_new;
     acc.w = acc.w * s_old + v.w * s_new;
     l = l * s_old + lk * s_new;
-    e = e * s_old + ek * s_new;
     m = mn;
   }
   part[cg][cq] = acc;
   if (cq == 0) {
     gmax[cg] = m;
     gsum[cg] = l;
-    gexact[cg] = e;
   }
   __syncthreads();
   if (t < QPR) {
     float M = kNegInf;
     for (int gi = 0; gi < CG; ++gi) M = fmaxf(M, gmax[gi]);
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f, Le = 0.f;
+    float L = 0.f;
     if (M != kNegInf) {
       for (int gi = 0; gi < CG; ++gi) {
         if (gmax[gi] == kNegInf) continue;
@@ -875,7 +878,6 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
         o.z += w * v.z;
         o.w += w * v.w;
         L += w * gsum[gi];
-        Le += w * gexact[gi];
       }
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -890,7 +892,7 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) orow[e] = __builtin_bit_cast(uint16_t, (__bf16)y[e]);
-    if (a.lse && t == 0) a.lse[bh * a.n + pos] = (Le > 0.f) ? (M + __log2f(Le)) * kLn2 : kNegInf;
+    if (a.lse && t == 0) a.lse[bh * a.n + pos] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
 }
 

@@ -324,8 +324,8 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  // l: sum of the bf16-rounded weights (the output's normaliser), e: of the unrounded ones (lse)
-  float ref = 0.f, l_run = 0.f, e_run = 0.f;
+  // l: sum of the bf16-rounded weights that multiply the value rows (the output's normaliser)
+  float ref = 0.f, l_run = 0.f;
   bool has = false;
   const float c2 = a.scale_log2;
   const float ninf = neg_inf();
@@ -429,10 +429,10 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16& u = sc[kb];
       uint32_t pk[8];
-      float part = 0.f, epart = 0.f;
+      float part = 0.f;
       auto exponentiate = [&]() {
         const float add = off - ref;
-        float la = 0.f, lb = 0.f, ea = 0.f;
+        float la = 0.f, lb = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = exp2_fast(__builtin_fmaf(u[r], mul, add));
@@ -441,10 +441,8 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
           // rounded weights, as the PV products use them
           if (r & 2) lb = add_bf16x2(pk[r >> 1], lb);
           else la = add_bf16x2(pk[r >> 1], la);
-          ea += p0 + p1;
         }
         part = la + lb;
-        epart = ea;
       };
       exponentiate();
       if (__builtin_amdgcn_ballot_w64(!has | !(part <= kTgFastWeightSum)) != 0ull) {
@@ -466,7 +464,6 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
           ref = nref;
           has = has || need;
           l_run *= alpha;
-          e_run *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -475,7 +472,6 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
         exponentiate();
       }
       l_run += part;
-      e_run += epart;
 #pragma unroll
       for (int gh = 0; gh < 2; ++gh) {
         const int g = 2 * kb + gh;
@@ -514,7 +510,6 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
 
   // epilogue: O = O^T / l, lse
   const float l_tot = l_run + __uint_as_float(__shfl_xor(__float_as_uint(l_run), 32));
-  const float e_tot = e_run + __uint_as_float(__shfl_xor(__float_as_uint(e_run), 32));
   if (!qok) return;
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   uint16_t* orow = a.out + (bh * a.n + qpos) * D;
@@ -529,7 +524,7 @@ __global__ __launch_bounds__(256) void tg_attn_kernel(TgArgs a) {
       *reinterpret_cast<u32x2*>(orow + d) = w;
     }
   if (a.lse && hh == 0)
-    a.lse[bh * a.n + qpos] = (e_tot > 0.f) ? (ref + __log2f(e_tot)) * kLn2 : neg_inf();
+    a.lse[bh * a.n + qpos] = (l_tot > 0.f) ? (ref + __log2f(l_tot)) * kLn2 : neg_inf();
 }
 
 }  // namespace

@@ -162,9 +162,8 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P,
       if (grid_g + p.grid_main > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
         return LONGATTN_ERR_UNSUPPORTED;
       a.grid_rows = (int)grid_g;
-      // partial outputs, then their (m, l, e) triples: reference, sum of the rounded weights,
-      // sum of the weights before rounding
-      p.part_floats = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 3);
+      // partial outputs, then their (m, l) pairs
+      p.part_floats = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2);
       p.ws_bytes = p.part_floats * sizeof(float);
     }
   } else if (for_forward) {

@@ -8,13 +8,15 @@ import sparse_long_sequence_banded_amd as la
 from workloads.torch_io import to_torch
 
 # Tolerances.  max-abs 2e-2 (bf16 I/O, fp32 accumulate) and 1e-4 (fp32) are the stated bars.
-# The tighter internal gates follow from the arithmetic: the kernels round P and the output to
-# bf16 (relative 2^-9 each), so the relative RMS error of a bf16 output stays well under 1e-2;
-# lse is computed from fp32 scores, so its error is far below 2e-3.
+# The tighter internal gates follow from the arithmetic: the bf16 kernels multiply the value rows
+# by softmax weights rounded to bf16 (round to nearest: relative error at most 2^-8 each) and
+# divide by the sum of those rounded weights, then round the output to bf16, so the relative RMS
+# error of a bf16 output stays well under 1e-2.  lse = ref + log2 of that same sum: its error is
+# at most ln(1 + 2^-8) = 3.9e-3 (reached when one key dominates a row), hence 4e-3.
 BF16_MAX_ABS = 2e-2
 BF16_REL_RMS = 1e-2
 F32_MAX_ABS = 1e-4
-LSE_ABS = {"bf16": 2e-3, "f32": 1e-4}
+LSE_ABS = {"bf16": 4e-3, "f32": 1e-4}
 
 
 def run_gpu(inp, device="cuda:0", want_lse=True):

@@ -140,16 +140,16 @@ def test_pointer_alignment_and_workspace_checks():
 
 
 def test_workspace_size_formula():
-    # global-row partials: B*H*g*chunks*(d+3) floats (the partial output row, its reference and
-    # its two weight sums; chunks of 1024 keys: 1000 keys -> 1, 3000 keys -> 3)
+    # global-row partials: B*H*g*chunks*(d+2) floats (the partial output row, its reference and
+    # its weight sum; chunks of 1024 keys: 1000 keys -> 1, 3000 keys -> 3)
     dg = _desc(batch=2, heads=3, n=1000, d=128, n_global=5, global_idx=FAKE)
-    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 1 * 131 * 4)
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 1 * 130 * 4)
     dg = _desc(batch=2, heads=3, n=3000, d=64, n_global=5, global_idx=FAKE)
-    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 3 * 67 * 4)
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 3 * 66 * 4)
     # a block layout's forward pass takes 512-key chunks: 1536 keys -> 3
     dl = _desc(batch=1, heads=2, n=1536, d=64, win_left=-1, win_right=-1, n_global=3,
                global_idx=FAKE, block_layout=FAKE, block=64, max_kb=3)
-    assert la.longattn_workspace_size(dl) == (la.LONGATTN_OK, 1 * 2 * 3 * 3 * 67 * 4)
+    assert la.longattn_workspace_size(dl) == (la.LONGATTN_OK, 1 * 2 * 3 * 3 * 66 * 4)
     assert la.longattn_workspace_size(_desc()) == (la.LONGATTN_OK, 0)
     f32 = _desc(dtype=la.LONGATTN_F32, n_global=5, global_idx=FAKE)
     assert la.longattn_workspace_size(f32) == (la.LONGATTN_OK, 0)

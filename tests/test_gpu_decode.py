@@ -118,7 +118,8 @@ def test_window_one_returns_the_new_value_rows():
 
 def test_decode_agrees_with_the_forward_pass():
     """The decode rows equal the corresponding rows of the library's own causal forward on the
-    whole sequence (within the bf16 tolerance: the two paths round differently)."""
+    whole sequence (within the bf16 tolerance: the two paths round differently; the forward's lse
+    is the log of its bf16-rounded weights' sum, within ln(1 + 2^-8) of the exact one)."""
     import torch
 
     n, window, m, d = 1100, 256, 4, 64
@@ -132,7 +133,7 @@ def test_decode_agrees_with_the_forward_pass():
                               win_right=0)
     torch.cuda.synchronize()
     assert (out_d.float() - out_f[:, :, n - m:].float()).abs().max().item() <= 2e-2
-    assert (lse_d - lse_f[:, :, n - m:]).abs().max().item() <= 2e-3
+    assert (lse_d - lse_f[:, :, n - m:]).abs().max().item() <= 4e-3
 
 
 def test_decode_full_size_sampled():

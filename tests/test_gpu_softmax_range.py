@@ -20,7 +20,8 @@ over the oracle's key sets shows that the inputs cross that bar:
   128 window walk, the global rows' key chunks and the listed layout blocks visit ascending
   blocks one after another).
 
-Tolerances are the stated bars (max-abs 2e-2 bf16, rel-RMS 1e-2, lse 2e-3).
+Tolerances are the stated bars (max-abs 2e-2 bf16) and the internal gates of gpu_helpers (rel-RMS
+1e-2, lse 4e-3).
 """
 
 import sys

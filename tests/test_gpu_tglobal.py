@@ -3,7 +3,8 @@
 Three comparisons: the global tokens' keys and values (side pass), the attention kernel on
 given global tokens (seeded bf16 side keys/values, so both sides read identical inputs), and the
 whole pipeline.  Tolerance, elementwise |gpu - oracle| <= atol + rtol * |oracle|, bf16 outputs:
-(2e-2, 1e-2); lse within 2e-3 (fp32 scores) for the attention on given global tokens.  End to
+(2e-2, 1e-2); lse within 4e-3 for the attention on given global tokens (lse is the log of the
+sum of the bf16-rounded weights, relative error at most 2^-8: ln(1 + 2^-8) = 3.9e-3).  End to
 end, the global tokens' keys are stored in bf16 before the attention reads them (relative error
 2^-9 per element), which moves a side score by up to scale * |q| |side_k| 2^-9 (about 0.016 for
 d = 64 with unit-variance rows); a row with few keys carries that into its lse, so the pipeline's
@@ -23,7 +24,7 @@ from workloads.tglobal import (TG_WORKLOADS, make_tglobal_inputs, tglobal_to_tor
 
 pytestmark = pytest.mark.gpu
 
-ATOL, RTOL, LSE_ATOL, LSE_ATOL_PIPELINE = 2e-2, 1e-2, 2e-3, 1e-2
+ATOL, RTOL, LSE_ATOL, LSE_ATOL_PIPELINE = 2e-2, 1e-2, 4e-3, 1e-2
 
 
 def _note(msg):
