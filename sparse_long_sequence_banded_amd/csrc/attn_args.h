@@ -36,7 +36,9 @@ struct FwdCore {
   float scale;            // softmax scale (> 0)
   float scale_log2;       // scale * log2(e)
   int tiles_per_b;        // main-kernel workgroups per batch sample
-  int uniform_dil;        // > 0: every head has this dilation, tiles_per_head = tile_off[1]
+  int uniform_dil;        // > 0: every head has this dilation
+  int head_tiles;         // > 0: every head takes this many main-kernel workgroups
+  int fair_from;          // workgroups with blockIdx.x >= fair_from take the balancing priority
 };
 
 // Passed by value to every kernel (kernarg segment, read through scalar loads).  Kernels that

@@ -109,11 +109,10 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
   if (gi < 0) {
     main_b = mi / a.tiles_per_b;
     int r = mi - main_b * a.tiles_per_b;
-    if (a.uniform_dil > 0) {
-      const int tph = args.tile_off[1];
-      main_h = r / tph;
-      r -= main_h * tph;
-      main_dl = a.uniform_dil;
+    if (a.head_tiles > 0) {
+      main_h = r / a.head_tiles;
+      r -= main_h * a.head_tiles;
+      main_dl = a.uniform_dil > 0 ? a.uniform_dil : args.dil[main_h];
     } else {
       int lo = 0, hi = a.H - 1;  // last head with tile_off[h] <= r
       while (lo < hi) {

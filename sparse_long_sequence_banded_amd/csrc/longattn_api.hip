@@ -144,12 +144,20 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P,
       a.tile_off[0] = 0;
       a.tile_off[1] = (int)th;
       per_b = th * a.H;
+      a.head_tiles = (int)th;
     } else {
+      // heads of different dilations often still take the same number of workgroups (n a
+      // multiple of dilation x rows per workgroup); the kernels then divide instead of searching
+      const long th0 = tiles_of_head(a.dil[0]);
+      bool same = true;
       a.tile_off[0] = 0;
       for (int h = 0; h < a.H; ++h) {
-        per_b += tiles_of_head(a.dil[h]);
+        const long th = tiles_of_head(a.dil[h]);
+        same = same && th == th0;
+        per_b += th;
         a.tile_off[h + 1] = (int)per_b;
       }
+      a.head_tiles = same ? (int)th0 : 0;
     }
     if (per_b * a.B > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
     a.tiles_per_b = (int)per_b;
