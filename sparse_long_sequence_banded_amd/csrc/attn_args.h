@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace longattn {
 
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
@@ -149,5 +152,34 @@ hipError_t launch_tglobal_side(const TgArgs& a, const uint16_t* x, const float* 
 hipError_t launch_tglobal_attention(const TgArgs& a, const float* tab_local,
                                     const float* tab_side, hipStream_t s);
 hipError_t launch_gate_lowrank(const GateArgs& a, hipStream_t s);
+
+// Host: workgroups of `kernel` (launched with `threads` threads) that the current device holds at
+// once over all its CUs, taken once per device into `cache` (one cache per kernel); 0 when the
+// runtime cannot say.
+constexpr int kMaxDevices = 64;
+inline long resident_capacity(const void* kernel, int threads,
+                              std::atomic<long> (&cache)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  long cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap > 0) return cap;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cap = (long)per_cu * cus;
+  cache[dev].store(cap, std::memory_order_relaxed);
+  return cap;
+}
+
+// Host: the first workgroup (by blockIdx.x) that takes the balancing priority.  Every workgroup
+// when the grid is a whole number of resident rounds (each round then ends at about the same time
+// on every CU), else the last round only (the earlier rounds keep the hardware's oldest-first
+// order, which spreads the remainder's workgroups over more CUs); none when the capacity is
+// unknown.
+inline int balancing_from(long grid, long cap) {
+  if (cap <= 0) return 0x7fffffff;
+  return grid % cap == 0 ? 0 : (int)std::max(0L, grid - cap);
+}
 
 }  // namespace longattn

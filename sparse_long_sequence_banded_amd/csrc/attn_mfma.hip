@@ -32,8 +32,6 @@
 // is read with the transposing 64-bit LDS read.  Both layouts XOR-swizzle 16-byte chunks by row
 // so that the reads of a wave hit distinct banks.
 
-#include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -132,13 +130,9 @@ void attn_fwd_kernel(FwdArgs args) {
     main_r = r;
   }
 
-  // Balancing priority.  The hardware issues the waves of the oldest workgroup on a SIMD first, so
-  // of the workgroups that share a CU the first one finishes in about half the time of the last,
-  // and in the final round of the grid the CU then runs with fewer and fewer workgroups.  A
-  // workgroup flagged by the host instead raises its waves' priority by the number of tiles it
-  // has left (3 with six or more, down to 0 for the last one): the workgroups of a CU progress
-  // together and finish together.  On a 4096-token window launch of one round this takes the
-  // kernel from 34.5 to 30.5 us, with the same results bit for bit.
+  // Workgroups flagged by the host raise their waves' priority by the number of tiles left (see
+  // balancing_priority): on a 4096-token window launch of one round this takes the kernel from
+  // 34.5 to 30.5 us, with the same results bit for bit.
   const bool fair = (int)blockIdx.x >= a.fair_from;
   if (fair) __builtin_amdgcn_s_setprio(3);
 
@@ -740,13 +734,7 @@ void attn_fwd_kernel(FwdArgs args) {
     if (n_tiles > 0) {
       int st = 0;  // stage of tile t
       for (int t = 0; t < n_tiles; ++t) {
-        if (fair) {
-          const int rem = n_tiles - t;
-          if (rem >= 6) __builtin_amdgcn_s_setprio(3);
-          else if (rem >= 4) __builtin_amdgcn_s_setprio(2);
-          else if (rem >= 2) __builtin_amdgcn_s_setprio(1);
-          else __builtin_amdgcn_s_setprio(0);
-        }
+        if (fair) balancing_priority(n_tiles - t);
         if constexpr (NS == 1) {
           if (t > 0) {
             __syncthreads();  // every wave is done with tile t-1: the stage may be refilled
@@ -916,36 +904,14 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   }
 }
 
-// Workgroups of `kernel` the current device holds at once over all its CUs, taken once per
-// device into `cache` (one cache per kernel); 0 when the runtime cannot say.
-constexpr int kMaxDevices = 64;
-long resident_capacity(const void* kernel, int threads, std::atomic<long> (&cache)[kMaxDevices]) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  long cap = cache[dev].load(std::memory_order_relaxed);
-  if (cap > 0) return cap;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  cap = (long)per_cu * cus;
-  cache[dev].store(cap, std::memory_order_relaxed);
-  return cap;
-}
-
 template <int D, int NW, int QB, int MODE>
 hipError_t launch_one(const FwdArgs& a0, long grid, hipStream_t s, const LaunchEvents& ev) {
   if (grid <= 0) return hipSuccess;
   static std::atomic<long> cap_cache[kMaxDevices];
   const long cap = resident_capacity(reinterpret_cast<const void*>(&attn_fwd_kernel<D, NW, QB, MODE>),
                                      NW * 64, cap_cache);
-  if (cap <= 0) return hipErrorInvalidDeviceFunction;
   FwdArgs a = a0;
-  // the balancing priority: every workgroup when the grid is a whole number of resident rounds
-  // (each round then ends at about the same time on every CU), else the last round only (the
-  // earlier rounds keep the hardware's oldest-first order, which spreads the remainder's
-  // workgroups over more CUs)
-  a.fair_from = (grid % cap == 0) ? 0 : (int)std::max(0L, grid - cap);
+  a.fair_from = balancing_from(grid, cap);
   if (ev.start || ev.stop)
     hipExtLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MODE>), dim3((unsigned)grid),
                           dim3(NW * 64), 0, s, ev.start, ev.stop, 0, a);

@@ -65,6 +65,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Logical workgroup id such that consecutive ids run on the same XCD.  Workgroups are handed to
 // the 8 XCDs round robin, so neighbouring query tiles (which re-read the same K/V rows) would
 // otherwise land in 8 different L2 caches.  This is a bijection on [0, G).
+// Balancing priority of a wave whose workgroup has `rem` key tiles left: 3 with six or more, 2
+// with four or five, 1 with two or three, 0 for the last one.  The hardware issues the waves of
+// the oldest workgroup on a SIMD first, so of the workgroups that share a CU the first finishes in
+// about half the time of the last, and in the final round of a grid the CU then runs with fewer
+// and fewer workgroups; with the priority the workgroups of a CU progress and finish together.
+__device__ __forceinline__ void balancing_priority(int rem) {
+  if (rem >= 6) __builtin_amdgcn_s_setprio(3);
+  else if (rem >= 4) __builtin_amdgcn_s_setprio(2);
+  else if (rem >= 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ int xcd_remap(int x, int G) {
   const int q = G >> 3, r = G & 7;
   const int xcd = x & 7, idx = x >> 3;
