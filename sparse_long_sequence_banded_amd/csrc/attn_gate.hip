@@ -158,19 +158,33 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
   const bool tok_ok = tok < tokens;
   const long tb = tok_ok ? tok / a.n : 0, ti = tok_ok ? tok % a.n : 0;
   const int Hd = a.H * a.d;
-  auto optr = [&](int e) -> uint16_t* {
-    return a.out + ((tb * a.H + e / a.d) * a.n + ti) * a.d + e % a.d;
-  };
   const int c0 = COLS * wave;
 
-  // ---- this wave's outputs: columns 16s + 8hh + {0..7} (8 consecutive elements stay in one
-  // head: d is a multiple of 16)
+  // ---- this wave's outputs: columns c0 + 16s + 8hh + {0..7} of the token (8 consecutive
+  // elements stay in one head: d is a multiple of 16).  Element e sits in head e / d at column
+  // e % d; the (head, column) pair is stepped by 16 columns per s rather than divided out, and
+  // the loads go out together.
+  uint16_t* orow[KSW];
+  {
+    const int e0 = c0 + 8 * hh;
+    int h = e0 / a.d, c = e0 - h * a.d;
+    uint16_t* tok_base = a.out + (tb * a.H * a.n + ti) * a.d;
+    const long head_stride = (long)a.n * a.d;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      orow[s] = tok_base + h * head_stride + c;
+      c += 16;
+      if (c >= a.d) {
+        c -= a.d;
+        ++h;
+      }
+    }
+  }
+  // a lane past the last token reads token 0's outputs (tb = ti = 0): they only enter that
+  // lane's own column of the products, and nothing of it is stored
   u32x4 of[KSW];
 #pragma unroll
-  for (int s = 0; s < KSW; ++s) {
-    of[s] = u32x4{0, 0, 0, 0};
-    if (tok_ok) of[s] = *reinterpret_cast<const u32x4*>(optr(c0 + 16 * s + 8 * hh));
-  }
+  for (int s = 0; s < KSW; ++s) of[s] = *reinterpret_cast<const u32x4*>(orow[s]);
   // ---- partial Z^T over this wave's columns
   f32x16 z[ZB];
 #pragma unroll
@@ -207,21 +221,28 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
 #pragma unroll
   for (int s = 0; s < R / 16; ++s)
     zf[s] = *reinterpret_cast<const u32x4*>(&zt[qj * ZROW + 16 * s + 8 * hh]);
+  // W_up fragments of 32-row block b (A operands), loaded one block ahead of their products
+  constexpr int NB = COLS / 32;
+  constexpr int RS = R / 16;
+  const uint16_t* wup = a.w_up + (long)(c0 + prow) * R + 8 * hh;
+  u32x4 wf[2][RS];
 #pragma unroll
-  for (int b = 0; b < COLS / 32; ++b) {
-    const int ob = c0 + 32 * b;
+  for (int s = 0; s < RS; ++s) wf[0][s] = *reinterpret_cast<const u32x4*>(wup + 16 * s);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b + 1 < NB) {
+#pragma unroll
+      for (int s = 0; s < RS; ++s)
+        wf[(b + 1) & 1][s] = *reinterpret_cast<const u32x4*>(wup + (long)32 * (b + 1) * R + 16 * s);
+    }
     f32x16 g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) g[r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < R / 16; ++s) {
-      const u32x4 aw =
-          *reinterpret_cast<const u32x4*>(a.w_up + (long)(ob + prow) * R + 16 * s + 8 * hh);
-      g = mfma_32x32x16(aw, zf[s], g);
-    }
+    for (int s = 0; s < RS; ++s) g = mfma_32x32x16(wf[b & 1][s], zf[s], g);
     if (!tok_ok) continue;
-    // registers 4q .. 4q+3: rows ob + 16(q/2) + 8hh + 4(q%2) + {0..3}, i.e. step 2b + q/2,
-    // slots 4(q%2) .. 4(q%2)+3
+    // registers 4q .. 4q+3: rows c0 + 32b + 16(q/2) + 8hh + 4(q%2) + {0..3}, i.e. step
+    // 2b + q/2, slots 4(q%2) .. 4(q%2)+3
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const u32x4& f = of[2 * b + (q >> 1)];
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
                          bf16_hi(w0) * sigmoid_fast(g[4 * q + 1]));
       w[1] = pack_bf16x2(bf16_lo(w1) * sigmoid_fast(g[4 * q + 2]),
                          bf16_hi(w1) * sigmoid_fast(g[4 * q + 3]));
-      *reinterpret_cast<u32x2*>(optr(ob + 16 * (q >> 1) + 8 * hh + 4 * (q & 1))) = w;
+      *reinterpret_cast<u32x2*>(orow[2 * b + (q >> 1)] + 4 * (q & 1)) = w;
     }
   }
 }
