@@ -37,6 +37,10 @@ def _parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="forward bench: untimed passes for about this long before the warm-up "
+                         "steps, so that the GPU runs at its steady clock when the timed region "
+                         "starts also with a short --warmup (reported as `settle`; 0 = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-passes", type=int, default=50,
                     help="forward (or decode) calls timed one by one after a read of a 512 MiB "
@@ -693,6 +697,17 @@ def main():
         if st != la.LONGATTN_OK:
             raise la.LongAttnError(st, "longattn_forward")
 
+    # clock settle: untimed passes for about --settle-ms (the GPU takes a few ms of back-to-back
+    # work to leave its idle clock; a short warm-up alone then overstates the step time by 10-15%)
+    settle_passes = 0
+    t_settle = time.perf_counter()
+    while args.settle_ms > 0 and (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        settle_passes += 50
+    settle = {"passes": settle_passes, "ms": round((time.perf_counter() - t_settle) * 1e3, 1)}
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -758,6 +773,7 @@ def main():
         "vs_baseline": None,
         "dtype": inp.dtype,
         "data": "synthetic",
+        "settle": settle,
         "config": {
             "workload": w.name,
             "batch": inp.batch, "heads": inp.heads, "seq_len": inp.n, "head_dim": inp.d,
@@ -768,6 +784,11 @@ def main():
             "description": w.note,
         },
         "pct_bf16_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        # which timing `value` is, and the flushed one beside it
+        "value_timing": "warm: wall clock over the K timed passes issued back to back, the device "
+                        "synchronized before and after; value_flushed is the median of single "
+                        "passes each timed after the L2 and MALL were flushed",
+        "value_flushed": cold["tflops_median"] if cold else None,
         "cold_l2_mall_flushed": cold,
         "kernels_ms": {"attention": round(attn_ms, 5),
                        "global_combine": round(comb_ms, 5) if inp.n_global else 0.0},
