@@ -128,12 +128,15 @@ __global__ __launch_bounds__(256) void gate_lowrank_kernel(GateArgs a) {
   }
 }
 
-// The same gate when H*d = 256*NW (NW <= 8) and r <= 128: one workgroup of NW waves gates 32
-// tokens, wave w owning the 256 output elements [256w, 256w + 256) of each token, so the
-// launch has a workgroup per 32 tokens.
-//   Z^T: wave w multiplies its 256 columns of W_down with its outputs (a split of the sum over
+// The same gate when H*d = COLS*NW (NW <= 8) and r <= 128: one workgroup of NW waves gates
+// TB blocks of 32 tokens, wave w owning the COLS output elements [COLS w, COLS w + COLS) of each
+// token, so the launch has a workgroup per 32 TB tokens.
+//   Z^T: wave w multiplies its COLS columns of W_down with its outputs (a split of the sum over
 //   H*d), and the NW partial sums are added through LDS, one 32-row block of Z^T at a time.
-//   G^T: wave w computes its 256 rows, then gates its own outputs.
+//   G^T: wave w computes its COLS rows, then gates its own outputs.
+// Each W_down and W_up fragment a wave loads serves its TB token blocks (two MFMAs at TB = 2),
+// so the weights, which every workgroup reads in full from L2 with 16-byte loads scattered over
+// 32 rows, cost half as much per token, and at 16K tokens the grid is one resident round.
 // In the first product a lane's eight k-slots of 16-column step s are the columns
 // 16s + 8hh + {0..7} (one 16-byte load each of outputs and of W_down).  In the second product
 // the order of the output rows within a 32-row block is free: A's row qj = 8q + 4h' + e is taken
@@ -141,38 +144,43 @@ __global__ __launch_bounds__(256) void gate_lowrank_kernel(GateArgs a) {
 // 16(q/2) + 8hh + 4(q%2) + {0..3}: exactly the columns that lane loaded in steps 2b and 2b + 1.
 // The outputs therefore stay in registers between the two products and are read from memory
 // once.
-template <int NW, int R, int COLS>
+template <int NW, int R, int COLS, int TB>
 __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a) {
   constexpr int ZB = R / 32;
   constexpr int KSW = COLS / 16;  // 16-column steps per wave
   constexpr int PSTR = 33;       // padded row of a partial block (floats)
   constexpr int ZROW = R + 8;    // padded token row of Z (bf16)
   constexpr int NT = NW * 64;
-  __shared__ float red[NW * 32 * PSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t zt[32 * ZROW];
+  __shared__ float red[TB][NW * 32 * PSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t zt[TB][32 * ZROW];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int qj = lane & 31, hh = lane >> 5;
   const long tokens = (long)a.B * a.n;
-  const long tok = (long)blockIdx.x * 32 + qj;  // this lane's token
-  const bool tok_ok = tok < tokens;
-  const long tb = tok_ok ? tok / a.n : 0, ti = tok_ok ? tok % a.n : 0;
   const int Hd = a.H * a.d;
   const int c0 = COLS * wave;
+  const long head_stride = (long)a.n * a.d;
 
-  // ---- this wave's outputs: columns c0 + 16s + 8hh + {0..7} of the token (8 consecutive
-  // elements stay in one head: d is a multiple of 16).  Element e sits in head e / d at column
-  // e % d; the (head, column) pair is stepped by 16 columns per s rather than divided out, and
-  // the loads go out together.
-  uint16_t* orow[KSW];
-  {
+  // ---- this wave's outputs of token block k: columns c0 + 16s + 8hh + {0..7} of the lane's
+  // token (8 consecutive elements stay in one head: d is a multiple of 16).  Element e sits in
+  // head e / d at column e % d; the (head, column) pair is stepped by 16 columns per s rather
+  // than divided out, and the loads go out together.  A lane past the last token reads token
+  // 0's outputs: they only enter that lane's own column of the products, and nothing of it is
+  // stored.
+  bool tok_ok[TB];
+  uint16_t* orow[TB][KSW];
+  u32x4 of[TB][KSW];
+#pragma unroll
+  for (int k = 0; k < TB; ++k) {
+    const long tok = ((long)blockIdx.x * TB + k) * 32 + qj;
+    tok_ok[k] = tok < tokens;
+    const long tb = tok_ok[k] ? tok / a.n : 0, ti = tok_ok[k] ? tok % a.n : 0;
     const int e0 = c0 + 8 * hh;
     int h = e0 / a.d, c = e0 - h * a.d;
     uint16_t* tok_base = a.out + (tb * a.H * a.n + ti) * a.d;
-    const long head_stride = (long)a.n * a.d;
 #pragma unroll
     for (int s = 0; s < KSW; ++s) {
-      orow[s] = tok_base + h * head_stride + c;
+      orow[k][s] = tok_base + h * head_stride + c;
       c += 16;
       if (c >= a.d) {
         c -= a.d;
@@ -180,47 +188,52 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
       }
     }
   }
-  // a lane past the last token reads token 0's outputs (tb = ti = 0): they only enter that
-  // lane's own column of the products, and nothing of it is stored
-  u32x4 of[KSW];
 #pragma unroll
-  for (int s = 0; s < KSW; ++s) of[s] = *reinterpret_cast<const u32x4*>(orow[s]);
-  // ---- partial Z^T over this wave's columns
-  f32x16 z[ZB];
+  for (int k = 0; k < TB; ++k)
 #pragma unroll
-  for (int zb = 0; zb < ZB; ++zb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) z[zb][r] = 0.f;
-#pragma unroll
-  for (int s = 0; s < KSW; ++s)
-#pragma unroll
-    for (int zb = 0; zb < ZB; ++zb) {
-      const u32x4 aw = *reinterpret_cast<const u32x4*>(a.w_down + (long)(32 * zb + qj) * Hd +
-                                                       c0 + 16 * s + 8 * hh);
-      z[zb] = mfma_32x32x16(aw, of[s], z[zb]);
-    }
-  // ---- Z^T = sum of the partials, one 32-row block at a time, stored as bf16 rows per token
+    for (int s = 0; s < KSW; ++s) of[k][s] = *reinterpret_cast<const u32x4*>(orow[k][s]);
+
+  // ---- Z^T = W_down O^T, one 32-row block at a time: this wave's partial sum over its columns
+  // for every token block, then the NW partials added through LDS and stored as bf16 rows per
+  // token
 #pragma unroll
   for (int zb = 0; zb < ZB; ++zb) {
-    float* mine = red + wave * 32 * PSTR;
+    f32x16 z[TB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * hh + (r & 3)) * PSTR + qj] = z[zb][r];
+    for (int k = 0; k < TB; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[k][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      const u32x4 aw = *reinterpret_cast<const u32x4*>(a.w_down + (long)(32 * zb + qj) * Hd +
+                                                       c0 + 16 * s + 8 * hh);
+#pragma unroll
+      for (int k = 0; k < TB; ++k) z[k] = mfma_32x32x16(aw, of[k][s], z[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      float* mine = red[k] + wave * 32 * PSTR;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * hh + (r & 3)) * PSTR + qj] = z[k][r];
+    }
     __syncthreads();
-    for (int e = tid; e < 32 * 32; e += NT) {
-      const int row = e & 31, t = e >> 5;
+    for (int e = tid; e < TB * 32 * 32; e += NT) {
+      const int k = e >> 10, row = e & 31, t = (e >> 5) & 31;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[w * 32 * PSTR + row * PSTR + t];
-      zt[t * ZROW + 32 * zb + row] = __builtin_bit_cast(uint16_t, (__bf16)v);
+      for (int w = 0; w < NW; ++w) v += red[k][w * 32 * PSTR + row * PSTR + t];
+      zt[k][t * ZROW + 32 * zb + row] = __builtin_bit_cast(uint16_t, (__bf16)v);
     }
     __syncthreads();
   }
   // ---- G^T for this wave's rows (A row qj is W_up row pi(qj) of the block), then the gate
   const int prow = 16 * (qj >> 4) + 8 * ((qj >> 2) & 1) + 4 * ((qj >> 3) & 1) + (qj & 3);
-  u32x4 zf[R / 16];
+  u32x4 zf[TB][R / 16];
 #pragma unroll
-  for (int s = 0; s < R / 16; ++s)
-    zf[s] = *reinterpret_cast<const u32x4*>(&zt[qj * ZROW + 16 * s + 8 * hh]);
+  for (int k = 0; k < TB; ++k)
+#pragma unroll
+    for (int s = 0; s < R / 16; ++s)
+      zf[k][s] = *reinterpret_cast<const u32x4*>(&zt[k][qj * ZROW + 16 * s + 8 * hh]);
   // W_up fragments of 32-row block b (A operands), loaded one block ahead of their products
   constexpr int NB = COLS / 32;
   constexpr int RS = R / 16;
@@ -235,35 +248,42 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
       for (int s = 0; s < RS; ++s)
         wf[(b + 1) & 1][s] = *reinterpret_cast<const u32x4*>(wup + (long)32 * (b + 1) * R + 16 * s);
     }
-    f32x16 g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) g[r] = 0.f;
+    for (int k = 0; k < TB; ++k) {
+      f32x16 g;
 #pragma unroll
-    for (int s = 0; s < RS; ++s) g = mfma_32x32x16(wf[b & 1][s], zf[s], g);
-    if (!tok_ok) continue;
-    // registers 4q .. 4q+3: rows c0 + 32b + 16(q/2) + 8hh + 4(q%2) + {0..3}, i.e. step
-    // 2b + q/2, slots 4(q%2) .. 4(q%2)+3
+      for (int r = 0; r < 16; ++r) g[r] = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4& f = of[2 * b + (q >> 1)];
-      const uint32_t w0 = (q & 1) ? f[2] : f[0], w1 = (q & 1) ? f[3] : f[1];
-      u32x2 w;
-      w[0] = pack_bf16x2(bf16_lo(w0) * sigmoid_fast(g[4 * q]),
-                         bf16_hi(w0) * sigmoid_fast(g[4 * q + 1]));
-      w[1] = pack_bf16x2(bf16_lo(w1) * sigmoid_fast(g[4 * q + 2]),
-                         bf16_hi(w1) * sigmoid_fast(g[4 * q + 3]));
-      *reinterpret_cast<u32x2*>(orow[2 * b + (q >> 1)] + 4 * (q & 1)) = w;
+      for (int s = 0; s < RS; ++s) g = mfma_32x32x16(wf[b & 1][s], zf[k][s], g);
+      if (!tok_ok[k]) continue;
+      // registers 4q .. 4q+3: rows c0 + 32b + 16(q/2) + 8hh + 4(q%2) + {0..3}, i.e. step
+      // 2b + q/2, slots 4(q%2) .. 4(q%2)+3
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4& f = of[k][2 * b + (q >> 1)];
+        const uint32_t w0 = (q & 1) ? f[2] : f[0], w1 = (q & 1) ? f[3] : f[1];
+        u32x2 w;
+        w[0] = pack_bf16x2(bf16_lo(w0) * sigmoid_fast(g[4 * q]),
+                           bf16_hi(w0) * sigmoid_fast(g[4 * q + 1]));
+        w[1] = pack_bf16x2(bf16_lo(w1) * sigmoid_fast(g[4 * q + 2]),
+                           bf16_hi(w1) * sigmoid_fast(g[4 * q + 3]));
+        *reinterpret_cast<u32x2*>(orow[k][2 * b + (q >> 1)] + 4 * (q & 1)) = w;
+      }
     }
   }
 }
 
+#ifndef GATE_TB
+#define GATE_TB 2
+#endif
 template <int NW, int COLS>
 hipError_t launch_split(const GateArgs& a, long tokens, hipStream_t s) {
-  const dim3 grid((unsigned)((tokens + 31) / 32)), block(NW * 64);
+  constexpr int TB = GATE_TB;  // 32-token blocks per workgroup
+  const dim3 grid((unsigned)((tokens + 32 * TB - 1) / (32 * TB))), block(NW * 64);
   switch (a.r) {
-    case 32: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 32, COLS>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 64, COLS>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 128, COLS>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 32, COLS, TB>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 64, COLS, TB>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((gate_lowrank_split_kernel<NW, 128, COLS, TB>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
