@@ -149,7 +149,6 @@ void attn_fwd_kernel(FwdArgs args) {
     constexpr int NLOAD = 2 * CH;      // 1 KB direct-load blocks per tile (K blocks, then V)
     constexpr int LPW = NLOAD / NW;    // of which each wave issues
     constexpr int RPB = 64 / CH;       // rows per 1 KB block
-    constexpr int GREG = (kGlobalCap + NT - 1) / NT;
     static_assert(NLOAD % NW == 0 && CH % LPW == 0, "each wave loads whole blocks of one matrix");
     static_assert(kGlobalCap % 64 == 0 && NT % 64 == 0, "global staging works in whole waves");
     constexpr bool kHasGlobalCols = MODE != kGlobalRows;
@@ -229,6 +228,37 @@ void attn_fwd_kernel(FwdArgs args) {
         }
       }
     }
+    // Q fragments (B operands of the score MFMAs, loaded once) and the global columns' positions.
+    // In layout mode both go out before the layout row is compacted, so the three loads' latencies
+    // overlap instead of following one another; the other modes load them after the key tiles
+    // are known, behind tile 0's loads.
+    constexpr int GREG = (kGlobalCap + NT - 1) / NT;
+    u32x4 qf[QB][KS];
+    int gx[GREG];
+    auto load_q = [&]() {
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          qf[qb][s] = u32x4{0, 0, 0, 0};
+          if (qpos[qb] >= 0)
+            qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
+        }
+    };
+    auto load_gx = [&]() {
+      if constexpr (kHasGlobalCols) {
+  #pragma unroll
+        for (int i = 0; i < GREG; ++i) {
+          const int c = tid + NT * i;
+          gx[i] = (a.g > 0 && c < a.g) ? gb[c] : a.n;
+        }
+      }
+    };
+    if constexpr (MODE == kLayout) {
+      load_gx();
+      load_q();
+    }
+
     // ------------------------------------------------------------------ key tiles
     int n_local = 0, k_lo = 0, k_hi = -1, tpb = 1;
     if constexpr (MODE == kBand) {
@@ -347,27 +377,11 @@ void attn_fwd_kernel(FwdArgs args) {
     // padding, loads a pad byte at each), then tile 0's loads go out when it is a local tile (it
     // needs nothing from the staging), so their latency overlaps that of the Q fragments and the
     // staging.
-    int gx[GREG];
-    if constexpr (kHasGlobalCols) {
-  #pragma unroll
-      for (int i = 0; i < GREG; ++i) {
-        const int c = tid + NT * i;
-        gx[i] = (n_gtiles > 0 && c < a.g) ? gb[c] : a.n;
-      }
-    }
+    if constexpr (MODE != kLayout) load_gx();
     if (n_local > 0) issue(kwave ? stage_k[0] : stage_v[0], tile_of(0));
 
-    // Q fragments (B operands of the score MFMAs), loaded once.
+    if constexpr (MODE != kLayout) load_q();
     const float c2 = a.scale_log2;
-    u32x4 qf[QB][KS];
-  #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        qf[qb][s] = u32x4{0, 0, 0, 0};
-        if (qpos[qb] >= 0)
-          qf[qb][s] = *reinterpret_cast<const u32x4*>(Qb + (long)qpos[qb] * D + 16 * s + 8 * hh);
-      }
 
     // ------------------------------------------------------------------ staging in LDS
     // Global-key columns: position and validity, once per workgroup.  A usable global key is
