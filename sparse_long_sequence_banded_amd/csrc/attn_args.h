@@ -153,14 +153,16 @@ hipError_t launch_tglobal_attention(const TgArgs& a, const float* tab_local,
                                     const float* tab_side, hipStream_t s);
 hipError_t launch_gate_lowrank(const GateArgs& a, hipStream_t s);
 
-// Host: workgroups of `kernel` (launched with `threads` threads) that the current device holds at
-// once over all its CUs, taken once per device into `cache` (one cache per kernel); 0 when the
-// runtime cannot say.
+// Host: workgroups of `kernel` (launched with `threads` threads) that the device owning `stream`
+// (the current device for the null stream) holds at once over all its CUs, taken once per device
+// into `cache` (one cache per kernel); 0 when the runtime cannot say.
 constexpr int kMaxDevices = 64;
-inline long resident_capacity(const void* kernel, int threads,
+inline long resident_capacity(const void* kernel, int threads, hipStream_t stream,
                               std::atomic<long> (&cache)[kMaxDevices]) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
   long cap = cache[dev].load(std::memory_order_relaxed);
   if (cap > 0) return cap;
   int per_cu = 0, cus = 0;

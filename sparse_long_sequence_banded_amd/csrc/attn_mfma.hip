@@ -923,7 +923,7 @@ hipError_t launch_one(const FwdArgs& a0, long grid, hipStream_t s, const LaunchE
   if (grid <= 0) return hipSuccess;
   static std::atomic<long> cap_cache[kMaxDevices];
   const long cap = resident_capacity(reinterpret_cast<const void*>(&attn_fwd_kernel<D, NW, QB, MODE>),
-                                     NW * 64, cap_cache);
+                                     NW * 64, s, cap_cache);
   FwdArgs a = a0;
   a.fair_from = balancing_from(grid, cap);
   if (ev.start || ev.stop)
