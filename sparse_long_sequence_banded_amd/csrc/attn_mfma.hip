@@ -83,28 +83,23 @@ struct Smem {
 };
 
 // One launch runs the main workgroups (MODE_MAIN) and the global-row partial workgroups
-// together, so the latency-bound global-row chunks overlap the main work.  Logical ids
-// (consecutive ids on one XCD) put one global-row workgroup in every three among the first
-// 3*grid_rows ids when the main grid is at least twice as large, else the global-row workgroups
-// first.  The work of one workgroup is a generic lambda over its kind (MODE) and its index wg
-// among that kind's workgroups; the kernel arguments stay in the kernel argument segment.
+// together.  The main workgroups take the first blockIdx.x values, remapped so that consecutive
+// main indices run on one XCD; the global-row workgroups come last in dispatch order, short
+// (512-key chunks) and many, so they fill the final round as main workgroups finish instead of
+// lengthening it.  The work of one workgroup is a generic lambda over its kind (MODE) and its
+// index wg among that kind's workgroups; the kernel arguments stay in the kernel argument
+// segment.
 template <int D, int NW, int QB, int MODE_MAIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 4 : 1)))
 void attn_fwd_kernel(FwdArgs args) {
   __shared__ Smem<D, stages_of(NW)> sm;
   const FwdCore a = args;
   const int total = gridDim.x;
-  const int Lid = xcd_remap(blockIdx.x, total);
   const int n_rows_wg = a.grid_rows;
   const int n_main_wg = total - n_rows_wg;
   int gi = -1, mi = 0;
-  if (n_main_wg >= 2 * n_rows_wg) {
-    if (Lid % 3 == 2 && Lid / 3 < n_rows_wg) gi = Lid / 3;
-    else mi = Lid - min(n_rows_wg, (Lid + 1) / 3);
-  } else {
-    if (Lid < n_rows_wg) gi = Lid;
-    else mi = Lid - n_rows_wg;
-  }
+  if ((int)blockIdx.x >= n_main_wg) gi = (int)blockIdx.x - n_main_wg;
+  else mi = xcd_remap(blockIdx.x, n_main_wg);
 
   // Main workgroups: batch sample, head, its dilation and the workgroup's index among the head's
   // workgroups, from the per-head workgroup table (read here, in the kernel body, so that the

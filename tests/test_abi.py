@@ -141,12 +141,14 @@ def test_pointer_alignment_and_workspace_checks():
 
 def test_workspace_size_formula():
     # global-row partials: B*H*g*chunks*(d+2) floats (the partial output row, its reference and
-    # its weight sum; chunks of 1024 keys: 1000 keys -> 1, 3000 keys -> 3)
-    dg = _desc(batch=2, heads=3, n=1000, d=128, n_global=5, global_idx=FAKE)
+    # its weight sum; the forward takes chunks of 512 keys: 500 keys -> 1, 1000 -> 2, 3000 -> 6)
+    dg = _desc(batch=2, heads=3, n=500, d=128, n_global=5, global_idx=FAKE)
     assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 1 * 130 * 4)
+    dg = _desc(batch=2, heads=3, n=1000, d=128, n_global=5, global_idx=FAKE)
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 2 * 130 * 4)
     dg = _desc(batch=2, heads=3, n=3000, d=64, n_global=5, global_idx=FAKE)
-    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 3 * 66 * 4)
-    # a block layout's forward pass takes 512-key chunks: 1536 keys -> 3
+    assert la.longattn_workspace_size(dg) == (la.LONGATTN_OK, 2 * 3 * 5 * 6 * 66 * 4)
+    # the same with a block layout: 1536 keys -> 3
     dl = _desc(batch=1, heads=2, n=1536, d=64, win_left=-1, win_right=-1, n_global=3,
                global_idx=FAKE, block_layout=FAKE, block=64, max_kb=3)
     assert la.longattn_workspace_size(dl) == (la.LONGATTN_OK, 1 * 2 * 3 * 3 * 66 * 4)

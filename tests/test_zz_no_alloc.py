@@ -87,7 +87,8 @@ def test_noalloc_matches_the_workspace_entry_point_twice_in_a_row():
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch():
-    # 64 heads x 256 global rows x 16 chunks x 66 floats = 69 MB of partials > 32 MiB
+    # 64 heads x 256 global rows x 32 chunks (of 512 keys) x 66 floats = 138 MB of partials,
+    # beyond the 32 MiB scratch
     desc = la.longattn_desc(batch=1, heads=64, n=16384, d=64, dtype=la.LONGATTN_BF16,
                             scale=0.125, win_left=256, win_right=256, dilation=None,
                             global_idx=ctypes.c_void_p(256).value, n_global=256, key_pad=None,
