@@ -11,8 +11,7 @@ namespace longattn {
 
 constexpr int kMaxTableHeads = 256;  // heads with individual dilations carried in the args
 constexpr int kKeyTile = 64;          // keys per K/V tile staged through LDS
-constexpr int kGlobalChunk = 1024;    // keys per global-row partial workgroup (backward)
-constexpr int kGlobalChunkFwd = 512;  // the same in the forward pass
+constexpr int kGlobalChunk = 512;     // keys (forward) or rows (backward) per global-row workgroup
 constexpr int kGlobalCap = 256;       // global tokens the bf16 kernels stage in LDS
 
 enum Mode : int { kBand = 0, kLayout = 1, kGlobalRows = 2 };

@@ -24,8 +24,9 @@
 // each edge counted once, as in the forward pass); window workgroups then walk the global rows
 // as gathered tiles (global keys for dQ, global query rows for dK/dV).  The owners that are global
 // tokens (global query rows for dQ, global keys for dK/dV) get their own workgroups, one per
-// (batch, head, 128 global rows, 1024-row chunk), which stream every position of the chunk and
-// write fp32 partial sums; a combine kernel adds the chunks and overwrites those rows.
+// (batch, head, 128 global rows, 512-row chunk), dispatched after the window workgroups so that
+// they fill the last round, which stream every position of the chunk and write fp32 partial
+// sums; a combine kernel adds the chunks and overwrites those rows.
 //
 // Block layouts (Big Bird reading notes, sections 3.2.2 and 3.3): a dQ workgroup owns a query
 // block and streams its listed key blocks; a dK/dV workgroup owns a key block and streams the
@@ -99,11 +100,11 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
   const FwdCore a = args;
   const BwdArgs gp = gargs;
   const int total = gridDim.x;
-  const int Lid = xcd_remap(blockIdx.x, total);
   const int n_glob_wg = a.grid_rows;
-  // global-owner workgroups first (they walk 1024-row chunks), then the window workgroups
-  const int gi = Lid < n_glob_wg ? Lid : -1;
-  const int mi = Lid - n_glob_wg;
+  const int n_main_wg = total - n_glob_wg;
+  // the window workgroups first (consecutive indices on one XCD), then the global owners
+  const int gi = (int)blockIdx.x >= n_main_wg ? (int)blockIdx.x - n_main_wg : -1;
+  const int mi = gi < 0 ? xcd_remap(blockIdx.x, n_main_wg) : 0;
 
   int main_b = 0, main_h = 0, main_dl = 1, main_r = 0;
   if (gi < 0) {

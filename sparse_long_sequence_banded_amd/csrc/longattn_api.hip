@@ -37,15 +37,17 @@ bool debug_enabled() {
   return e && e[0] == '1';
 }
 
-// Keys per global-row partial workgroup of the forward pass: 512.  The global-row workgroups are
-// dispatched after all the main ones, so they fill the last round as main workgroups finish, and
-// shorter ones fill it more evenly (window mode, global rows last: 512 keys against 1024 made the
-// attention kernel 4.7% faster on the 16K dilated workload and 8.6% on the 4K one, for 0.5 us
-// more in the combine; 384, 640 and 768 fell in between; a 64-row block layout: 7% faster).  The
-// backward keeps 1024.
+// Keys per global-row partial workgroup of the forward pass (rows per global-owner workgroup of
+// the backward): 512.  Those workgroups are dispatched after all the main ones, so they fill the
+// last round as main workgroups finish, and shorter ones fill it more evenly.  Forward, window
+// mode, 512 keys against 1024: the attention kernel 4.7% faster on the 16K dilated workload and
+// 8.6% on the 4K one, for 0.5 us more in the combine (384, 640 and 768 fell in between; a 64-row
+// block layout: 7% faster).  Backward, 512 rows with the owners last against 1024 first: the 4K
+// window workload 11% and the 4K block layout 16% faster, the 16K ones unchanged (256 and 384:
+// slower).
 int forward_chunk_keys(const longattn_desc* d) {
   (void)d;
-  return kGlobalChunkFwd;
+  return kGlobalChunk;
 }
 
 longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P,

@@ -292,11 +292,11 @@ def test_backward_workspace_and_pointer_checks():
 
 def test_backward_matrix_core_workspace_formula():
     # bf16, d in {64, 128}, no layout: Drow and lse2 per row (padded to 4 floats each) plus the
-    # global rows' partials: 3 * B*H*g*chunks*d floats (chunks of 1024 rows)
+    # global rows' partials: 3 * B*H*g*chunks*d floats (chunks of 512 rows: 1001 rows -> 2)
     d = _desc(batch=2, heads=3, n=1001, d=64, n_global=5, global_idx=FAKE)
     rows_pad = (2 * 3 * 1001 + 3) // 4 * 4
     assert la.longattn_backward_workspace_size(d) == (la.LONGATTN_OK,
-                                                      (2 * rows_pad + 3 * 2 * 3 * 5 * 1 * 64) * 4)
+                                                      (2 * rows_pad + 3 * 2 * 3 * 5 * 2 * 64) * 4)
     d = _desc(batch=1, heads=2, n=3000, d=128)
     assert la.longattn_backward_workspace_size(d) == (la.LONGATTN_OK, 2 * 6000 * 4)
     # a layout of 64- or 128-blocks alone also runs on matrix cores ...
