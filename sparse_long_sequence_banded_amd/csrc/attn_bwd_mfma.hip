@@ -759,7 +759,9 @@ __global__ __launch_bounds__(3 * D) void bwd_global_combine_kernel(FwdArgs args,
   const float* po = which == 0 ? a.part + slot0 * D + col
                                : a.part + slots * D + slot0 * 2 * D + (which - 1) * D + col;
   const long stride = which == 0 ? D : 2 * D;
+  // the loads of sixteen chunks go out together; the sum keeps the chunk order
   float s = 0.f;
+#pragma unroll 16
   for (int k = 0; k < a.chunks; ++k) s += po[k * stride];
   uint16_t* dst = static_cast<uint16_t*>(which == 0 ? gp.dq : which == 1 ? gp.dk : gp.dv) +
                   (bh * a.n + pos) * D + col;
