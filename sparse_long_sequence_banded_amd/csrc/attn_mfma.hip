@@ -859,20 +859,33 @@ __global__ __launch_bounds__(kCombineThreads) void global_combine_kernel(FwdArgs
   const int cg = t / QPR, cq = t % QPR;
   float m = kNegInf, l = 0.f;                 // running max and normaliser of this thread
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int k = cg; k < K; k += CG) {
-    const float mk = pml[2 * k];
-    const float lk = pml[2 * k + 1];
-    const float4 v = *reinterpret_cast<const float4*>(po + (long)k * D + 4 * cq);
-    if (mk == kNegInf) continue;  // chunk with no key: o = 0, l = 0
-    const float mn = fmaxf(m, mk);
-    const float s_old = (m == kNegInf) ? 0.f : exp2f(m - mn), s_new = exp2f(mk - mn);
-    acc.x = acc.x * s_old + v.x * s_new;
-    acc.y = acc.y * s_old + v.y * s_new;
-    acc.z = acc.z * s_old + v.z * s_new;
-    acc.w = acc.w * s_old + v.w * s_new;
-    l = l * s_old + lk * s_new;
-    m = mn;
+  // This thread's chunks k = cg, cg + CG, ... in batches of KB whose loads all go out before any
+  // is used (an index past the last chunk reads the last one and is then skipped), merged in
+  // chunk order.
+  constexpr int KB = 4;
+  for (int k0 = cg; k0 < K; k0 += KB * CG) {
+    float mk[KB], lk[KB];
+    float4 v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = min(k0 + u * CG, K - 1);
+      mk[u] = pml[2 * k];
+      lk[u] = pml[2 * k + 1];
+      v[u] = *reinterpret_cast<const float4*>(po + (long)k * D + 4 * cq);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      // past the last chunk, or a chunk with no key (o = 0, l = 0)
+      if (k0 + u * CG >= K || mk[u] == kNegInf) continue;
+      const float mn = fmaxf(m, mk[u]);
+      const float s_old = (m == kNegInf) ? 0.f : exp2f(m - mn), s_new = exp2f(mk[u] - mn);
+      acc.x = acc.x * s_old + v[u].x * s_new;
+      acc.y = acc.y * s_old + v[u].y * s_new;
+      acc.z = acc.z * s_old + v[u].z * s_new;
+      acc.w = acc.w * s_old + v[u].w * s_new;
+      l = l * s_old + lk[u] * s_new;
+      m = mn;
+    }
   }
   part[cg][cq] = acc;
   if (cq == 0) {
