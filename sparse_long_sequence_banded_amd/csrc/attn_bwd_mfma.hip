@@ -741,31 +741,47 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
 }
 
 // Adds the chunk partials of every global token and writes its dQ row (the global query row)
-// and its dK and dV rows (the global key): one workgroup of 3D threads per (batch, head, global
-// token); thread t sums column t % D of one of the three over the chunks.
+// and its dK and dV rows (the global key).  A workgroup of 192 threads takes 256 / D global
+// tokens; thread t sums the column quad of one of the three that it owns over the chunks.
 template <int D>
-__global__ __launch_bounds__(3 * D) void bwd_global_combine_kernel(FwdArgs args, BwdArgs gp) {
+__global__ __launch_bounds__(192) void bwd_global_combine_kernel(FwdArgs args, BwdArgs gp) {
+  constexpr int QPR = D / 4;           // column quads per row
+  constexpr int TPR = 3 * QPR;         // threads per global token
+  constexpr int RPW = 192 / TPR;       // global tokens per workgroup
+  static_assert(RPW * TPR == 192, "whole tokens per workgroup");
   const FwdCore a = args;
   const int t = threadIdx.x;
-  const long row = blockIdx.x;
+  const long rows = (long)a.B * a.H * a.g;
+  const long row = (long)blockIdx.x * RPW + t / TPR;
+  if (row >= rows) return;  // no barrier follows
   const long bh = row / a.g;
   const int c = (int)(row - bh * a.g);
   const int b = (int)(bh / a.H);
   const int pos = a.gidx[(long)b * a.g + c];
   if (pos < 0 || pos >= a.n) return;
-  const int which = t / D, col = t % D;  // 0: dQ, 1: dK, 2: dV
+  const int which = (t % TPR) / QPR, col = 4 * (t % QPR);  // 0: dQ, 1: dK, 2: dV
   const long slots = (long)a.B * a.H * a.g * a.chunks;
   const long slot0 = (bh * a.g + c) * a.chunks;
   const float* po = which == 0 ? a.part + slot0 * D + col
                                : a.part + slots * D + slot0 * 2 * D + (which - 1) * D + col;
   const long stride = which == 0 ? D : 2 * D;
-  // the loads of sixteen chunks go out together; the sum keeps the chunk order
-  float s = 0.f;
+  // the loads of sixteen chunks go out together; the sums keep the chunk order
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 16
-  for (int k = 0; k < a.chunks; ++k) s += po[k * stride];
+  for (int k = 0; k < a.chunks; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(po + k * stride);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const float f = which == 2 ? 1.f : a.scale;
+  u32x2 w;
+  w[0] = pack_bf16x2(which == 2 ? s.x : s.x * f, which == 2 ? s.y : s.y * f);
+  w[1] = pack_bf16x2(which == 2 ? s.z : s.z * f, which == 2 ? s.w : s.w * f);
   uint16_t* dst = static_cast<uint16_t*>(which == 0 ? gp.dq : which == 1 ? gp.dk : gp.dv) +
                   (bh * a.n + pos) * D + col;
-  *dst = __builtin_bit_cast(uint16_t, (__bf16)(which == 2 ? s : s * a.scale));
+  *reinterpret_cast<u32x2*>(dst) = w;
 }
 
 // dK and dV as two passes (each recomputes the scores; the dK pass also dP) where the fused
@@ -801,7 +817,8 @@ hipError_t launch_bwd_d(const FwdArgs& a, const BwdArgs& g, long grid, hipStream
   }
   const long grows = (long)a.B * a.H * a.g;
   if (grows > 0)
-    timed(2, bwd_global_combine_kernel<D>, dim3((unsigned)grows), dim3(3 * D), a, g);
+    timed(2, bwd_global_combine_kernel<D>, dim3((unsigned)((grows * D + 255) / 256)), dim3(192),
+          a, g);
   else if (ev && (hipEventRecord(ev[2].start, s) != hipSuccess ||
                   hipEventRecord(ev[2].stop, s) != hipSuccess))
     return hipErrorUnknown;
