@@ -161,7 +161,8 @@ __global__ __launch_bounds__(64) void tg_project_kernel(TgArgs a, const uint16_t
   // W rows are read from column c0 on, y rows from row r0 on; out-of-range reads give zeros
   const u32x4 wrs = buf_rsrc((is_v ? wv : wk) + c0,
                              (uint32_t)(((long)a.dm * HD - c0) * 2));
-  const u32x4 yrs = buf_rsrc(y + r0 * a.dm, (uint32_t)((rows - r0) * a.dm * 2));
+  const u32x4 yrs =
+      buf_rsrc(y + r0 * a.dm, (uint32_t)(std::min(rows - r0, (long)kProjTile) * a.dm * 2));
   const uint32_t ws_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ws[0][0]));
   const uint32_t ys_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ys[0][0]));
   const int vi = lane & 15, vg = lane >> 4;
@@ -211,12 +212,23 @@ __global__ __launch_bounds__(64) void tg_project_kernel(TgArgs a, const uint16_t
   if (col >= HD) return;
   const int h = col / a.D, c = col % a.D;
   uint16_t* dst = is_v ? a.sv_out : a.sk_out;
+  // (batch, global token) of the tile's first row, then stepped: one division per lane instead
+  // of a 64-bit division per element (measured 10.0 -> 8.5 us at 1024 global tokens; a
+  // 64 x 64 tile per four-wave workgroup with the whole 512-deep product staged at once, or a
+  // second accumulation chain, gained nothing more)
+  const int rbase = (int)r0;  // B * G < 2^31
+  const int b0 = rbase / a.G, g0 = rbase - b0 * a.G;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const long row = r0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-    if (row >= rows) continue;
-    const long b = row / a.G, g = row % a.G;
-    dst[((b * a.H + h) * a.G + g) * a.D + c] = __builtin_bit_cast(uint16_t, (__bf16)acc[r]);
+    const int off = 8 * (r >> 2) + 4 * hh + (r & 3);
+    if (rbase + off >= rows) continue;
+    int b = b0, g = g0 + off;
+    while (g >= a.G) {  // at most 31 / G + 1 steps
+      g -= a.G;
+      ++b;
+    }
+    dst[(((long)b * a.H + h) * a.G + g) * a.D + c] =
+        __builtin_bit_cast(uint16_t, (__bf16)acc[r]);
   }
 }
 

@@ -295,6 +295,11 @@ longattn_status plan_tglobal(const longattn_tglobal_desc* d, TgPlan* P) {
     return LONGATTN_ERR_UNSUPPORTED;
   const long tiles = ((long)d->n + 127) / 128;
   if ((long)d->batch * d->heads * tiles > 0x7fffffffL) return LONGATTN_ERR_UNSUPPORTED;
+  // the projections address W [d_model][heads*d] with 32-bit byte offsets and count the global
+  // tokens of all samples in int32
+  if ((long)d->d_model * d->heads * d->d * 2 > 0x7fffffffL ||
+      (long)d->batch * std::max(1, d->n / d->block) > 0x7fffffffL - 64)
+    return LONGATTN_ERR_UNSUPPORTED;
   TgPlan& p = *P;
   p = TgPlan();
   TgArgs& a = p.a;

@@ -347,6 +347,8 @@ def _tdesc(**kw):
     (dict(d=96), la.LONGATTN_ERR_UNSUPPORTED),
     (dict(radius=513), la.LONGATTN_ERR_UNSUPPORTED),
     (dict(max_distance=600), la.LONGATTN_ERR_UNSUPPORTED),
+    # W [d_model][heads * d] must stay under 2^31 bytes
+    (dict(heads=1 << 16, d=128, d_model=128), la.LONGATTN_ERR_UNSUPPORTED),
 ])
 def test_bad_tglobal_descriptors_are_rejected(kw, status):
     d = _tdesc(**kw)
