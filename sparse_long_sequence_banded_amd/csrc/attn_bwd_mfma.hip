@@ -210,11 +210,11 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
       }
     }
     // ------------------------------------------------------------------ streamed tiles
-    int n_local = 0, s_lo = 0, s_hi = -1, tpb = 1;
+    int n_local = 0, s_lo = 0, s_hi = -1;
+    constexpr int TPB = QT / kKeyTile;  // layout mode: key tiles per block (QT rows)
     if constexpr (MODE == kLayout) {
       // dQ: the valid key blocks listed for this query block; dK/dV: the query blocks whose
       // layout row lists this key block, in ascending order (compacted by wave 0)
-      tpb = a.block / kKeyTile;
       const int nb = a.n / a.block;
       const int me = o0 / a.block;
       if (wave == 0) {
@@ -245,7 +245,7 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
         if (lane == 0) sm.lay_cnt = base;
       }
       __syncthreads();
-      n_local = sm.lay_cnt * tpb;
+      n_local = sm.lay_cnt * TPB;
     } else if constexpr (MODE == kBand) {
       if (a.band_on) {
         const int o_last = min(o0 + QT, np) - 1;
@@ -288,7 +288,7 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
         T.count = min(kKeyTile, np - T.ks0);
       } else if constexpr (MODE == kLayout) {
         T.gathered = 0;
-        T.base = sm.lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
+        T.base = sm.lay_list[t / TPB] * a.block + (t % TPB) * kKeyTile;
         T.count = kKeyTile;
       } else {
         T.gathered = 0;

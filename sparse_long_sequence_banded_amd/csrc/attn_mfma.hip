@@ -255,7 +255,8 @@ void attn_fwd_kernel(FwdArgs args) {
     }
 
     // ------------------------------------------------------------------ key tiles
-    int n_local = 0, k_lo = 0, k_hi = -1, tpb = 1;
+    int n_local = 0, k_lo = 0, k_hi = -1;
+    constexpr int TPB = QT / kKeyTile;  // layout mode: key tiles per block (QT rows)
     if constexpr (MODE == kBand) {
       if (a.band_on) {
         const int q_last = min(q0 + QT, np) - 1;
@@ -264,7 +265,6 @@ void attn_fwd_kernel(FwdArgs args) {
         n_local = (k_hi >= k_lo) ? (k_hi - k_lo + kKeyTile) / kKeyTile : 0;
       }
     } else if constexpr (MODE == kLayout) {
-      tpb = a.block / kKeyTile;
       if (wave == 0) {  // compact the valid block ids of this row into LDS
         const int nb = a.n / a.block;
         const int* row = a.layout + ((long)h * nb + q0 / a.block) * a.max_kb;
@@ -280,7 +280,7 @@ void attn_fwd_kernel(FwdArgs args) {
         if (lane == 0) lay_cnt = base;
       }
       __syncthreads();
-      n_local = lay_cnt * tpb;
+      n_local = lay_cnt * TPB;
     } else {
       const int c0 = ck * a.chunk_keys;
       const int c1 = min(a.n, c0 + a.chunk_keys);
@@ -322,7 +322,7 @@ void attn_fwd_kernel(FwdArgs args) {
       } else if constexpr (MODE == kLayout) {
         T.gathered = 0;
         T.lt = t;
-        T.base = lay_list[t / tpb] * a.block + (t % tpb) * kKeyTile;
+        T.base = lay_list[t / TPB] * a.block + (t % TPB) * kKeyTile;
         T.count = kKeyTile;
       } else {
         T.gathered = 0;
