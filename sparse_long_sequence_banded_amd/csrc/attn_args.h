@@ -41,6 +41,7 @@ struct FwdCore {
   int uniform_dil;        // > 0: every head has this dilation
   int head_tiles;         // > 0: every head takes this many main-kernel workgroups
   int fair_from;          // workgroups with blockIdx.x >= fair_from take the balancing priority
+  int rows_by_xcd;        // global-row workgroups take the heads their XCD's main work ended on
 };
 
 // Passed by value to every kernel (kernarg segment, read through scalar loads).  Kernels that

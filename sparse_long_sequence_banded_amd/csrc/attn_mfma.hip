@@ -166,13 +166,31 @@ void attn_fwd_kernel(FwdArgs args) {
     int b = 0, h = 0, dl = 1, p = 0, np = a.n, q0 = 0, ck = 0, rg = 0;
     if constexpr (MODE == kGlobalRows) {
       const int rgs = (a.g + QT - 1) / QT;
-      int x = wg;
-      ck = x % a.chunks;
-      x /= a.chunks;
-      rg = x % rgs;
-      x /= rgs;
-      h = x % a.H;
-      b = x / a.H;
+      if (a.rows_by_xcd) {
+        // Every (batch, head) takes the same number of main workgroups and the main grid and
+        // the (batch, head) count are multiples of 8, so XCD x (blockIdx.x % 8) has run the
+        // main work of pairs x*hpx .. x*hpx + hpx - 1, in that order.  Its global-row
+        // workgroups (wg % 8 == x) take those pairs' chunks, the most recent pair first and its
+        // chunks from the last keys down, which its L2 may still hold (reads below L2 on the
+        // 16K dilated workload 169 -> 159 MB, 1-2.5% faster on the three workloads with global
+        // tokens).  Any order gives the same results.
+        const int per = rgs * a.chunks;    // workgroups per (batch, head)
+        const int hpx = (a.B * a.H) >> 3;  // (batch, head) pairs per XCD
+        const int s = wg >> 3, i = s / per, u = s - i * per;
+        const int bhx = (wg & 7) * hpx + hpx - 1 - i;
+        b = bhx / a.H;
+        h = bhx - b * a.H;
+        rg = u / a.chunks;
+        ck = a.chunks - 1 - (u - rg * a.chunks);
+      } else {
+        int x = wg;
+        ck = x % a.chunks;
+        x /= a.chunks;
+        rg = x % rgs;
+        x /= rgs;
+        h = x % a.H;
+        b = x / a.H;
+      }
     } else {
       (void)wg;
       b = main_b;

@@ -175,6 +175,9 @@ longattn_status plan_call(const longattn_desc* d, bool for_forward, Plan* P,
       if (grid_g + p.grid_main > 0x7fffffffL || (long)a.B * a.H * a.g > 0x7fffffffL)
         return LONGATTN_ERR_UNSUPPORTED;
       a.grid_rows = (int)grid_g;
+      // global-row workgroups may follow the XCDs' main work when it splits evenly over them
+      a.rows_by_xcd =
+          (a.head_tiles > 0 && ((long)a.B * a.H) % 8 == 0 && p.grid_main % 8 == 0) ? 1 : 0;
       // partial outputs, then their (m, l) pairs
       p.part_floats = (size_t)a.B * a.H * a.g * a.chunks * (size_t)(d->d + 2);
       p.ws_bytes = p.part_floats * sizeof(float);

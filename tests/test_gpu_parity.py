@@ -249,6 +249,22 @@ def test_window_tiles_in_rotated_order_with_global_keys_inside(wl, wr):
     assert gpu_count(inp) == oracle.count_inputs(inp)
 
 
+@pytest.mark.parametrize("d,block", [(64, 0), (128, 0), (64, 64)])
+def test_global_rows_ordered_by_xcd(d, block):
+    # eight (batch, head) pairs that take equal main work, so the global-row workgroups take the
+    # heads whose main work their XCD ran, most recent first and chunks from the last keys down;
+    # 150 global rows make two (window) or three (64-row blocks) row groups per head, over three
+    # key chunks; any order of that work must give the oracle's result
+    if block:
+        inp = random_case(48, batch=2, heads=4, n=1280, d=d, block=block, max_kb=3,
+                          n_global=150, pad="random", pad_count=40)
+    else:
+        inp = random_case(47 + d, batch=2, heads=4, n=1300, d=d, win_left=100, win_right=60,
+                          n_global=150, pad="random", pad_count=40)
+    parity(inp, f"global rows by XCD d={d} block={block}")
+    assert gpu_count(inp) == oracle.count_inputs(inp)
+
+
 def test_uniform_and_per_head_dilation_tables():
     for dil in (3, [1, 2, 3, 4, 5]):
         inp = random_case(37, batch=1, heads=5, n=900, d=64, win_left=17, win_right=9,
