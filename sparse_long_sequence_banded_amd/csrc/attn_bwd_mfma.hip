@@ -155,13 +155,27 @@ void attn_bwd_kernel(FwdArgs args, BwdArgs gargs) {
     int b = 0, h = 0, dl = 1, p = 0, np = a.n, o0 = 0, ck = 0, rg = 0;
     if constexpr (MODE == kGlobalRows) {
       const int rgs = (a.g + QT - 1) / QT;
-      int x = wg;
-      ck = x % a.chunks;
-      x /= a.chunks;
-      rg = x % rgs;
-      x /= rgs;
-      h = x % a.H;
-      b = x / a.H;
+      if (a.rows_by_xcd) {
+        // as in the forward: XCD x (blockIdx.x % 8) ran the main work of (batch, head) pairs
+        // x*hpx .. x*hpx + hpx - 1 in order; its global-owner workgroups take those pairs, the
+        // most recent first, chunks from the last rows down
+        const int per = rgs * a.chunks;
+        const int hpx = (a.B * a.H) >> 3;
+        const int s = wg >> 3, i = s / per, u = s - i * per;
+        const int bhx = (wg & 7) * hpx + hpx - 1 - i;
+        b = bhx / a.H;
+        h = bhx - b * a.H;
+        rg = u / a.chunks;
+        ck = a.chunks - 1 - (u - rg * a.chunks);
+      } else {
+        int x = wg;
+        ck = x % a.chunks;
+        x /= a.chunks;
+        rg = x % rgs;
+        x /= rgs;
+        h = x % a.H;
+        b = x / a.H;
+      }
     } else {
       (void)wg;
       b = main_b;

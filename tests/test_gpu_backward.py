@@ -171,6 +171,20 @@ def test_layout_backward_with_globals_and_padding(block, d):
 
 
 # ------------------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("d,block", [(64, 0), (128, 0), (64, 64)])
+def test_global_owners_ordered_by_xcd(d, block):
+    # eight (batch, head) pairs with equal main work: the global-owner workgroups take the heads
+    # whose main work their XCD ran, in reverse order; 150 global tokens give two (window) or
+    # three (64-row blocks) owner groups per head over three chunks
+    if block:
+        inp = random_case(58, batch=2, heads=4, n=1280, d=d, block=block, max_kb=3,
+                          n_global=150, pad="random", pad_count=40)
+    else:
+        inp = random_case(57 + d, batch=2, heads=4, n=1300, d=d, win_left=100, win_right=60,
+                          n_global=150, pad="random", pad_count=40)
+    check(inp, 59, f"global owners by XCD d={d} block={block}")
+
+
 def test_window_zero_sends_the_gradient_to_v():
     inp = random_case(75, batch=2, heads=2, n=300, d=64, win_left=0, win_right=0,
                       dilations=[1, 2])
