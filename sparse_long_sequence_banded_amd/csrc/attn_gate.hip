@@ -148,10 +148,12 @@ template <int NW, int R, int COLS, int TB>
 __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a) {
   constexpr int ZB = R / 32;
   constexpr int KSW = COLS / 16;  // 16-column steps per wave
-  constexpr int PSTR = 33;       // padded row of a partial block (floats)
+  // partial blocks are stored token-major: a token's 32 rows, padded to 36 floats so that the
+  // 16-byte writes of 16 consecutive tokens hit distinct banks
+  constexpr int TSTR = 36;
   constexpr int ZROW = R + 8;    // padded token row of Z (bf16)
   constexpr int NT = NW * 64;
-  __shared__ float red[TB][NW * 32 * PSTR];
+  __shared__ __attribute__((aligned(16))) float red[TB][NW * 32 * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t zt[TB][32 * ZROW];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -234,17 +236,32 @@ __global__ __launch_bounds__(NW * 64) void gate_lowrank_split_kernel(GateArgs a)
     }
 #pragma unroll
     for (int k = 0; k < TB; ++k) {
-      float* mine = red[k] + wave * 32 * PSTR;
+      // registers 4j .. 4j+3 are rows 8j + 4hh + {0..3} of token qj
+      float* mine = red[k] + (wave * 32 + qj) * TSTR + 4 * hh;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * hh + (r & 3)) * PSTR + qj] = z[k][r];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(mine + 8 * j) =
+            make_float4(z[k][4 * j], z[k][4 * j + 1], z[k][4 * j + 2], z[k][4 * j + 3]);
     }
     __syncthreads();
-    for (int e = tid; e < TB * 32 * 32; e += NT) {
-      const int k = e >> 10, row = e & 31, t = (e >> 5) & 31;
-      float v = 0.f;
+    // thread e adds rows 4(e%8) .. +3 of token (e/8)%32 over the waves (in wave order) and stores
+    // them as four bf16 (16-byte reads and 8-byte writes instead of one word at a time: 27.7 ->
+    // 27.4 us at 16K tokens x 1024 x r 128, 27.3 -> 26.2 us at 32K tokens x 512, same bits)
+    for (int e = tid; e < TB * 32 * 8; e += NT) {
+      const int k = e >> 8, t = (e >> 3) & 31, j4 = e & 7;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[k][w * 32 * PSTR + row * PSTR + t];
-      zt[k][t * ZROW + 32 * zb + row] = __builtin_bit_cast(uint16_t, (__bf16)v);
+      for (int w = 0; w < NW; ++w) {
+        const float4 p = *reinterpret_cast<const float4*>(red[k] + (w * 32 + t) * TSTR + 4 * j4);
+        v.x += p.x;
+        v.y += p.y;
+        v.z += p.z;
+        v.w += p.w;
+      }
+      u32x2 zw;
+      zw[0] = pack_bf16x2(v.x, v.y);
+      zw[1] = pack_bf16x2(v.z, v.w);
+      *reinterpret_cast<u32x2*>(&zt[k][t * ZROW + 32 * zb + 4 * j4]) = zw;
     }
     __syncthreads();
   }
