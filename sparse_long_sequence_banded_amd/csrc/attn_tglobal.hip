@@ -67,11 +67,13 @@ __global__ void tg_bias_kernel(TgArgs a, const float* tab_local, const float* ta
 
 // Block sums and RMS norm: y[b][g][c] (bf16) and side_valid[b][g].  One wave per (b, g); lane l
 // sums the 8-column groups l, l + 64, ... (KPG groups) over the block's rows with 16-byte loads,
-// ROWS rows at a time with every load in flight (a padded row is read and weighted by 0).
+// ROWS rows at a time with every load in flight (a padded row is read and weighted by 0; with
+// one group per lane, 16 rows: a default 16-token block in one round of loads, global-token pass
+// 12.5 -> 12.3 us at d_model 512, same bits).
 template <int KPG>
 __global__ __launch_bounds__(64) void tg_aggregate_kernel(TgArgs a, const uint16_t* x,
                                                          const float* gamma, uint16_t* y) {
-  constexpr int ROWS = KPG <= 2 ? 8 : (KPG == 4 ? 4 : 2);
+  constexpr int ROWS = KPG == 1 ? 16 : (KPG == 2 ? 8 : (KPG == 4 ? 4 : 2));
   const int g = blockIdx.x % a.G;
   const int b = blockIdx.x / a.G;
   const int lane = threadIdx.x;
