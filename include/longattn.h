@@ -50,7 +50,7 @@ extern "C" {
 typedef enum longattn_status {
   LONGATTN_OK = 0,
   LONGATTN_ERR_INVALID_ARG = 1, /* a size, window, dilation, index or pointer is out of range */
-  LONGATTN_ERR_UNSUPPORTED = 2, /* valid, but this build has no kernel for it (see below)     */
+  LONGATTN_ERR_UNSUPPORTED = 2, /* valid, but the library has no kernel for it (see below)    */
   LONGATTN_ERR_ALIGNMENT = 3,   /* q, k, v or out is not 16-byte aligned                       */
   LONGATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than longattn_workspace_size  */
   LONGATTN_ERR_HIP = 5          /* the HIP runtime reported an error while launching           */
